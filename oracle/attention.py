@@ -1,0 +1,158 @@
+"""Plain fp64 CPU oracle for exact attention and its gradients.
+
+TEST INFRASTRUCTURE ONLY.  This module is imported by the tests, by the smoke
+check and by the benchmark's CPU-baseline leg, never by the library.  It shares
+no code with the HIP path; both read their inputs from the seeded generators in
+exact_io_aware_51_amd.workloads, which hold no attention arithmetic.
+
+What is computed (all in float64, one (batch, head) slice at a time):
+
+* Forward -- the definition softmax(Q K^T / sqrt(d)) V with the optional causal
+  mask ("How Flash Attention Works: Tiling, Softmax, GPU I/O", section "How
+  Flash Attention Works: The Exact-Attention Idea"; "attn-flash-equivalence",
+  section "Standard attention I/O is the bottleneck", which lists the three
+  materialising steps S = QK^T/sqrt(d_k), P = softmax(S), O = P V).  The score
+  matrix S and the probability matrix P are materialised, exactly as the naive
+  pipeline does; this is the plain definition, not the tiled algorithm.
+  The scale is an argument (the kernels receive it as an fp32 number).
+  Causal mask: key j is visible to query i iff j <= i.
+  Side output: the per-row log-sum-exp LSE_i = ln sum_j exp(S_ij), i.e. the
+  "compact per-row statistics" the backward pass needs ("How Flash Attention
+  Works", section "The Backward Pass: Recomputation Instead of Stored
+  Activations"), folded into one number per row (running max m plus ln of the
+  normaliser l).
+
+* Backward -- the pages give no formulas; this is the chain rule applied to the
+  same definition, with P recomputed from S:
+      dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+      dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+
+For long sequences the forward materialises S and P in panels of whole rows;
+every row is still formed and normalised in one piece, and rows never interact,
+so the panel size changes no arithmetic.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x):
+    """Accept numpy arrays or torch tensors (any float dtype) and return float64 numpy."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        import torch  # local: only when torch tensors are passed
+        x = x.to(torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(q, k, scale, causal, row0=0):
+    """Rows row0 .. row0+len(q)-1 of S = scale * q k^T, masked entries = -inf."""
+    s = scale * (q @ k.T)
+    if causal:
+        rows = np.arange(row0, row0 + q.shape[0])[:, None]
+        cols = np.arange(k.shape[0])[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    return s
+
+
+def _softmax_rows(s):
+    """Row softmax of s and each row's log-sum-exp.
+
+    The row max is subtracted before exponentiating; it cancels in the ratio
+    and only keeps exp() in range.
+    """
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=1, keepdims=True)
+    return e / l, (m + np.log(l))[:, 0]
+
+
+def attention_probs(q, k, scale, causal):
+    """P = softmax(scale * q k^T [+ mask]) for one head: q, k are [N, d]."""
+    q, k = _f64(q), _f64(k)
+    p, _ = _softmax_rows(_scores(q, k, scale, causal))
+    return p
+
+
+def _forward_head(q, k, v, scale, causal, panel_rows):
+    n = q.shape[0]
+    o = np.empty((n, v.shape[1]))
+    lse = np.empty(n)
+    for r0 in range(0, n, panel_rows):
+        r1 = min(n, r0 + panel_rows)
+        p, lse[r0:r1] = _softmax_rows(_scores(q[r0:r1], k, scale, causal, row0=r0))
+        o[r0:r1] = p @ v
+    return o, lse
+
+
+def attention_forward(q, k, v, scale, causal, panel_rows=2048):
+    """O = softmax(scale * Q K^T [+ causal mask]) V and LSE, for [B, H, N, d] inputs.
+
+    Returns (O [B,H,N,d] float64, LSE [B,H,N] float64, natural log).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, _ = q.shape
+    o = np.empty(q.shape[:3] + (v.shape[3],))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = _forward_head(q[b, h], k[b, h], v[b, h], scale, causal, panel_rows)
+    return o, lse
+
+
+def attention_forward_rows(q, k, v, scale, causal, b, h, rows):
+    """O and LSE for selected query rows of one (b, h) slice (for spot checks at full size).
+
+    Row i needs only q_i and all keys/values: O_i = sum_j P_ij v_j with P_i = softmax(S_i).
+    """
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+    rows = [int(i) for i in rows]
+    o = np.empty((len(rows), vh.shape[1]))
+    lse = np.empty(len(rows))
+    for t, i in enumerate(rows):
+        p, lse[t:t + 1] = _softmax_rows(_scores(qh[i:i + 1], kh, scale, causal, row0=i))
+        o[t] = (p @ vh)[0]
+    return o, lse
+
+
+def _backward_head(q, k, v, do, scale, causal):
+    p, _ = _softmax_rows(_scores(q, k, scale, causal))
+    dv = p.T @ do
+    dp = do @ v.T
+    dsum = np.sum(p * dp, axis=1, keepdims=True)
+    ds = p * (dp - dsum)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, scale, causal, heads=None):
+    """dQ, dK, dV of L = sum(dO * O) for [B, H, N, d] inputs (float64).
+
+    heads: optional list of (b, h) pairs; only those slices are computed and the
+    result is a dict {(b, h): (dq, dk, dv)}.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    if heads is not None:
+        return {(b, h): _backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+                for (b, h) in heads}
+    dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(v.shape)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            dq[b, h], dk[b, h], dv[b, h] = _backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+    return dq, dk, dv
+
+
+def attention_backward_rows(q, k, v, do, scale, causal, b, h, rows):
+    """dQ for selected query rows of one (b, h) slice.
+
+    Row i of dQ needs only row i of P and dP: dQ_i = scale * sum_j P_ij (dP_ij - D_i) k_j.
+    """
+    qh, kh, vh, doh = (_f64(x[b, h]) for x in (q, k, v, do))
+    out = np.empty((len(rows), kh.shape[1]))
+    for t, i in enumerate(list(rows)):
+        p, _ = _softmax_rows(_scores(qh[i:i + 1], kh, scale, causal, row0=i))
+        dp = doh[i:i + 1] @ vh.T
+        ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        out[t] = scale * (ds @ kh)[0]
+    return out

@@ -1,0 +1,55 @@
+"""Plant plausible mistakes in copies of the oracle and check a pin catches each.
+
+The mistakes are planted in the oracle's own source text (on the CPU), never in
+the HIP path.  Every mutant must fail at least one pin; a mutant that survives
+would mean the pins cannot tell that mistake from the definition.
+"""
+import os
+import types
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "attention.py")
+
+MUTANTS = {
+    "dropped scale": ("s = scale * (q @ k.T)", "s = (q @ k.T)"),
+    "transposed operand": ("s = scale * (q @ k.T)", "s = scale * (k @ q.T)"),
+    "mask direction": ("cols > rows", "cols < rows"),
+    "mask off by one": ("cols > rows", "cols >= rows"),
+    "mask ignores panel offset": ("np.arange(row0, row0 + q.shape[0])", "np.arange(0, q.shape[0])"),
+    "lse without max": ("(m + np.log(l))[:, 0]", "(np.log(l))[:, 0]"),
+    "unnormalised P": ("return e / l, (m", "return e, (m"),
+    "max along wrong axis": ("np.max(s, axis=1, keepdims=True)", "np.max(s, axis=0, keepdims=True)"),
+    "sum along wrong axis": ("l = np.sum(e, axis=1, keepdims=True)", "l = np.sum(e, axis=0, keepdims=True)"),
+    "dV not transposed": ("dv = p.T @ do", "dv = p @ do"),
+    "dP uses K": ("dp = do @ v.T", "dp = do @ k.T"),
+    "dropped D term": ("ds = p * (dp - dsum)", "ds = p * dp"),
+    "D wrong axis": ("dsum = np.sum(p * dp, axis=1, keepdims=True)", "dsum = np.sum(p * dp, axis=0, keepdims=True)"),
+    "dQ missing scale": ("dq = scale * (ds @ k)", "dq = (ds @ k)"),
+    "dK not transposed": ("dk = scale * (ds.T @ q)", "dk = scale * (ds @ q)"),
+    "dK sign": ("dk = scale * (ds.T @ q)", "dk = -scale * (ds.T @ q)"),
+    "dQ uses V": ("dq = scale * (ds @ k)", "dq = scale * (ds @ v)"),
+    "output uses K": ("o[r0:r1] = p @ v", "o[r0:r1] = p @ k"),
+}
+
+
+def _mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"pattern not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)  # noqa: S102
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _mutant(*MUTANTS[name])
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # AssertionError, or a crash caused by the mistake
+            failures.append(f"{pin.__name__}: {type(e).__name__}")
+    assert failures, f"no pin catches the planted mistake '{name}'"
