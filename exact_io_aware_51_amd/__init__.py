@@ -1,0 +1,150 @@
+"""Python binding of libfa, the gfx950 fused exact-attention library.
+
+The functions named like the C entry points (fa_fwd, fa_bwd,
+fa_bwd_workspace_bytes, fa_status_string, fa_version) take raw device
+addresses and sizes exactly as include/fa.h declares them.  forward() and
+backward() are conveniences for torch tensors: they check shapes, allocate the
+outputs with torch, pass data_ptr()s and torch's current HIP stream, and raise
+FaError on a non-zero status.  All arithmetic happens in the HIP kernels; there
+is no CPU or PyTorch fallback, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes",
+           "fa_status_string", "fa_version", "forward", "backward", "library_path", "load"]
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status}: {fa_status_string(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by exact_io_aware_51_amd.build); raise if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_51_amd.build` "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _LIB = lib
+    return lib
+
+
+# ------------------------------------------------------------------ raw C ABI
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal,
+           dtype, stream) -> int:
+    return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                         scale, causal, dtype, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
+    return load().fa_bwd_workspace_bytes(B, H, N, d, dtype)
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(status).decode()
+
+
+def fa_version() -> int:
+    return load().fa_version()
+
+
+# ------------------------------------------------------------ torch helpers
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check(*ts):
+    import torch
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError("tensors must live on a HIP device (no CPU path exists)")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (, o, dout) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _stream(t, stream):
+    import torch
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def forward(q, k, v, scale=None, causal=False, out=None, lse=None, need_lse=True, stream=None):
+    """O, LSE = softmax(scale q k^T [+ causal mask]) v on the GPU.  scale defaults to 1/sqrt(d)."""
+    import torch
+    _check(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    if need_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                lse.data_ptr() if lse is not None else None, B, H, N, d, scale, int(bool(causal)),
+                _dtype_code(q), _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, stream=None):
+    """dQ, dK, dV of sum(dout * o) on the GPU, recomputing the score tiles from lse."""
+    import torch
+    _check(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                B, H, N, d, scale, int(bool(causal)), code, _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

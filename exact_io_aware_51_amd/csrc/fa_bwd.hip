@@ -1,0 +1,443 @@
+// fa_bwd.hip -- backward pass of fused exact attention for gfx950.
+//
+// Only O and the per-row log-sum-exp were kept by the forward pass; the score
+// tiles are recomputed here tile by tile from Q, K and LSE, never read from
+// device memory ("How Flash Attention Works: Tiling, Softmax, GPU I/O",
+// section "The Backward Pass: Recomputation Instead of Stored Activations").
+// The gradient formulas are the chain rule on O = softmax(scale Q K^T) V:
+//   P = exp(scale S - LSE),  dV = P^T dO,  dP = dO V^T,
+//   D_i = sum_c dO_ic O_ic (= sum_j P_ij dP_ij),  dS = P (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// Three kernels, all deterministic (no atomics):
+//   bwd_pre  : D_i, one pass over dO and O (bound by device memory);
+//   bwd_dkdv : a workgroup owns 128 keys (32 per wave, K and V rows in VGPRs)
+//              and streams query tiles (Q, dO, LSE, D) through LDS,
+//              accumulating dK^T and dV^T on the matrix cores;
+//   bwd_dq   : a workgroup owns 128 queries (Q and dO rows in VGPRs) and
+//              streams key tiles (K, V) through LDS, accumulating dQ^T.
+// Every product keeps the owned rows as the accumulator's lane column, feeds
+// the recomputed P or dS back from registers as a B operand, and reads the
+// other operand transposed out of LDS (see fa_device.h).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;
+  int N;
+  int nblk;    // blocks per head along the owned dimension
+  int total;   // workgroups in the grid
+  float c;     // scale * log2(e), signed
+  float scale;
+};
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdOwn = 128;   // owned rows per workgroup (32 per wave)
+constexpr int kBwdTile = 64;   // streamed rows per tile
+
+// --------------------------------------------------------------------------
+// D_i = sum_c dO_ic * O_ic, fp32.  LPR lanes cooperate on one row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                      float* __restrict__ dvec, long long rows) {
+  constexpr int EPL = 16 / sizeof(T);  // elements per lane (one 16-byte chunk)
+  constexpr int LPR = D / EPL;         // lanes per row
+  constexpr int RPB = 256 / LPR;       // rows per block
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * RPB + tid / LPR;
+  const int part = tid % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const size_t off = (size_t)row * D + part * EPL;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + off);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + off);
+    typedef T TV __attribute__((ext_vector_type(EPL)));
+    const TV av = __builtin_bit_cast(TV, a), bv = __builtin_bit_cast(TV, b);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf((float)av[e], (float)bv[e], acc);
+  }
+#pragma unroll
+  for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, LPR);
+  if (row < rows && part == 0) dvec[row] = acc;
+}
+
+template <typename T, int D>
+struct BwdLayout {
+  static constexpr int ROWB = D * (int)sizeof(T);
+  static constexpr int STR = D + (sizeof(T) == 2 ? 8 : 2);  // LDS row stride, elements
+  static constexpr int TILE = kBwdTile * STR;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int PER_THREAD = kBwdTile * CPR / kBwdThreads;
+  static_assert(kBwdTile * CPR % kBwdThreads == 0, "tile chunks must split evenly");
+  static constexpr int LDS_BYTES = 2 * 2 * TILE * (int)sizeof(T) + 2 * 2 * kBwdTile * 4;
+};
+
+// --------------------------------------------------------------------------
+// dK, dV for 128 keys per workgroup.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using M = Mma<T>;
+  using L = BwdLayout<T, D>;
+  using Frag = typename M::Frag;
+  constexpr int KSTEPS = D / M::KS;
+  constexpr int MB = D / 32;
+  constexpr int PSTEPS = 32 / M::KS;
+
+  __shared__ __attribute__((aligned(16))) char smem[L::LDS_BYTES];
+  T* lds_q = reinterpret_cast<T*>(smem);          // [2][TILE]
+  T* lds_do = lds_q + 2 * L::TILE;                 // [2][TILE]
+  float* lds_lse = reinterpret_cast<float*>(lds_do + 2 * L::TILE);  // [2][64], log2 units
+  float* lds_d = lds_lse + 2 * kBwdTile;                            // [2][64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int N = a.N;
+
+  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bh = bid / a.nblk;
+  const int kblk = bid - bh * a.nblk;
+  const int kb0 = kblk * kBwdOwn;
+  const int kw = kb0 + 32 * wave;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
+  const T* __restrict__ Kp = reinterpret_cast<const T*>(a.k) + head;
+  const T* __restrict__ Vp = reinterpret_cast<const T*>(a.v) + head;
+  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + head;
+  const float* __restrict__ lse = a.lse + (size_t)bh * N;
+  const float* __restrict__ dvec = a.dvec + (size_t)bh * N;
+
+  // K and V rows of this lane's key column, as B fragments (k = d).
+  Frag kf[KSTEPS], vf[KSTEPS];
+  {
+    const int key = kw + col;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      kf[ks] = key < N ? row_frag<T>(Kp + (size_t)key * D + ks * M::KS, h) : zero_frag<T>();
+      vf[ks] = key < N ? row_frag<T>(Vp + (size_t)key * D + ks * M::KS, h) : zero_frag<T>();
+    }
+  }
+
+  const int ntiles = (N + kBwdTile - 1) / kBwdTile;
+  const int first = CAUSAL ? kb0 / kBwdTile : 0;
+
+  u32x4 qreg[L::PER_THREAD], doreg[L::PER_THREAD];
+  float lse_r = 0.0f, d_r = 0.0f;
+  auto load_tile = [&](int j) {
+    const int i0 = j * kBwdTile;
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int c = tid + i * kBwdThreads;
+      const int row = c / L::CPR, cc = c - row * L::CPR;
+      const int qi = i0 + row;
+      if (qi < N) {
+        const size_t off = (size_t)qi * D + cc * (16 / sizeof(T));
+        qreg[i] = *reinterpret_cast<const u32x4*>(Q + off);
+        doreg[i] = *reinterpret_cast<const u32x4*>(dO + off);
+      } else {
+        qreg[i] = u32x4{0u, 0u, 0u, 0u};
+        doreg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < kBwdTile) {
+      const int qi = i0 + tid;
+      lse_r = qi < N ? lse[qi] * kLog2e : 0.0f;
+      d_r = qi < N ? dvec[qi] : 0.0f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int c = tid + i * kBwdThreads;
+      const int row = c / L::CPR, cc = c - row * L::CPR;
+      const int e = cc * (16 / sizeof(T));
+      *reinterpret_cast<u32x4*>(lds_q + buf * L::TILE + row * L::STR + e) = qreg[i];
+      *reinterpret_cast<u32x4*>(lds_do + buf * L::TILE + row * L::STR + e) = doreg[i];
+    }
+    if (tid < kBwdTile) {
+      lds_lse[buf * kBwdTile + tid] = lse_r;
+      lds_d[buf * kBwdTile + tid] = d_r;
+    }
+  };
+
+  f32x16 dkacc[MB], dvacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    dkacc[mb] = f32x16{};
+    dvacc[mb] = f32x16{};
+  }
+  const float c = a.c;
+  const int mykey = kw + col;
+
+  if (first < ntiles) {
+    load_tile(first);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int j = first; j < ntiles; ++j) {
+    const int buf = (j - first) & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    const int i0 = j * kBwdTile;
+    // waves whose keys all follow this tile's last query have nothing to do
+    if (!CAUSAL || i0 + kBwdTile - 1 >= kw) {
+      const T* qt = lds_q + buf * L::TILE;
+      const T* dot = lds_do + buf * L::TILE;
+      const float* lt = lds_lse + buf * kBwdTile;
+      const float* dt = lds_d + buf * kBwdTile;
+      const bool edge = (i0 + kBwdTile > N) || (CAUSAL && i0 < kw + 31);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const T* qrow = qt + (32 * qb + col) * L::STR;
+        const T* dorow = dot + (32 * qb + col) * L::STR;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          s = M::mma(row_frag<T>(qrow + ks * M::KS, h), kf[ks], s);
+          dp = M::mma(row_frag<T>(dorow + ks * M::KS, h), vf[ks], dp);
+        }
+        // s: rows = queries i0 + 32 qb + acc_row(r, h), column = key mykey
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int rr = 32 * qb + 8 * g + 4 * h;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rr);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * g + u;
+            float p = fast_exp2(__builtin_fmaf(s[r], c, -l4[u]));
+            if (edge) {
+              const int qi = i0 + rr + u;
+              const bool ok = qi < N && (!CAUSAL || mykey <= qi);
+              p = ok ? p : 0.0f;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[u]);
+          }
+        }
+        // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over this block's 32 queries)
+#pragma unroll
+        for (int t = 0; t < PSTEPS; ++t) {
+          const Frag pf = acc_frag<T>(s, t);
+          const Frag sf = acc_frag<T>(dp, t);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            dvacc[mb] = M::mma(trans_frag<T>(dot, L::STR, 32 * qb, t, 32 * mb, lane), pf, dvacc[mb]);
+            dkacc[mb] = M::mma(trans_frag<T>(qt, L::STR, 32 * qb, t, 32 * mb, lane), sf, dkacc[mb]);
+          }
+        }
+      }
+    }
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (mykey < N) {
+    T* dkrow = reinterpret_cast<T*>(a.dk) + head + (size_t)mykey * D;
+    T* dvrow = reinterpret_cast<T*>(a.dv) + head + (size_t)mykey * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * mb + 8 * g + 4 * h;
+        store4<T>(dkrow + d0, dkacc[mb][4 * g] * sc, dkacc[mb][4 * g + 1] * sc, dkacc[mb][4 * g + 2] * sc,
+                  dkacc[mb][4 * g + 3] * sc);
+        store4<T>(dvrow + d0, dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2], dvacc[mb][4 * g + 3]);
+      }
+  }
+}
+
+// --------------------------------------------------------------------------
+// dQ for 128 queries per workgroup.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+  using M = Mma<T>;
+  using L = BwdLayout<T, D>;
+  using Frag = typename M::Frag;
+  constexpr int KSTEPS = D / M::KS;
+  constexpr int MB = D / 32;
+  constexpr int PSTEPS = 32 / M::KS;
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * L::TILE * sizeof(T)];
+  T* lds_k = reinterpret_cast<T*>(smem);  // [2][TILE]
+  T* lds_v = lds_k + 2 * L::TILE;          // [2][TILE]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int N = a.N;
+
+  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bh = bid / a.nblk;
+  int qb = bid - bh * a.nblk;
+  if (CAUSAL) qb = a.nblk - 1 - qb;
+  const int q0 = qb * kBwdOwn;
+  const int qw = q0 + 32 * wave;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
+  const T* __restrict__ Kp = reinterpret_cast<const T*>(a.k) + head;
+  const T* __restrict__ Vp = reinterpret_cast<const T*>(a.v) + head;
+  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + head;
+
+  const int myq = qw + col;
+  Frag qf[KSTEPS], dof[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
+    dof[ks] = myq < N ? row_frag<T>(dO + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
+  }
+  const float lse2 = myq < N ? a.lse[(size_t)bh * N + myq] * kLog2e : 0.0f;
+  const float dq_d = myq < N ? a.dvec[(size_t)bh * N + myq] : 0.0f;
+
+  const int ntiles_all = (N + kBwdTile - 1) / kBwdTile;
+  int ntiles = ntiles_all;
+  if (CAUSAL) {
+    const int last = (q0 + kBwdOwn - 1) / kBwdTile + 1;
+    ntiles = last < ntiles_all ? last : ntiles_all;
+  }
+
+  u32x4 kreg[L::PER_THREAD], vreg[L::PER_THREAD];
+  auto load_tile = [&](int j) {
+    const int k0 = j * kBwdTile;
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int c = tid + i * kBwdThreads;
+      const int row = c / L::CPR, cc = c - row * L::CPR;
+      const int key = k0 + row;
+      if (key < N) {
+        const size_t off = (size_t)key * D + cc * (16 / sizeof(T));
+        kreg[i] = *reinterpret_cast<const u32x4*>(Kp + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(Vp + off);
+      } else {
+        kreg[i] = u32x4{0u, 0u, 0u, 0u};
+        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < L::PER_THREAD; ++i) {
+      const int c = tid + i * kBwdThreads;
+      const int row = c / L::CPR, cc = c - row * L::CPR;
+      const int e = cc * (16 / sizeof(T));
+      *reinterpret_cast<u32x4*>(lds_k + buf * L::TILE + row * L::STR + e) = kreg[i];
+      *reinterpret_cast<u32x4*>(lds_v + buf * L::TILE + row * L::STR + e) = vreg[i];
+    }
+  };
+
+  f32x16 dqacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) dqacc[mb] = f32x16{};
+  const float c = a.c;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1);
+    const int k0 = j * kBwdTile;
+    if (!CAUSAL || k0 <= qw + 31) {
+      const T* kt = lds_k + buf * L::TILE;
+      const T* vt = lds_v + buf * L::TILE;
+      const bool edge = (k0 + kBwdTile > N) || (CAUSAL && k0 + kBwdTile - 1 > qw);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const T* krow = kt + (32 * kb + col) * L::STR;
+        const T* vrow = vt + (32 * kb + col) * L::STR;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          s = M::mma(row_frag<T>(krow + ks * M::KS, h), qf[ks], s);
+          dp = M::mma(row_frag<T>(vrow + ks * M::KS, h), dof[ks], dp);
+        }
+        // s^T: rows = keys k0 + 32 kb + acc_row(r, h), column = query myq
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+          if (edge) {
+            const int key = k0 + 32 * kb + acc_row(r, h);
+            const bool ok = key < N && (!CAUSAL || key <= myq);
+            p = ok ? p : 0.0f;
+          }
+          dp[r] = p * (dp[r] - dq_d);
+        }
+        // dQ^T += K^T dS^T  (contraction over this block's 32 keys)
+#pragma unroll
+        for (int t = 0; t < PSTEPS; ++t) {
+          const Frag sf = acc_frag<T>(dp, t);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            dqacc[mb] = M::mma(trans_frag<T>(kt, L::STR, 32 * kb, t, 32 * mb, lane), sf, dqacc[mb]);
+        }
+      }
+    }
+    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (myq < N) {
+    T* dqrow = reinterpret_cast<T*>(a.dq) + head + (size_t)myq * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * mb + 8 * g + 4 * h;
+        store4<T>(dqrow + d0, dqacc[mb][4 * g] * sc, dqacc[mb][4 * g + 1] * sc, dqacc[mb][4 * g + 2] * sc,
+                  dqacc[mb][4 * g + 3] * sc);
+      }
+  }
+}
+
+// --------------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.H * p.N;
+  {
+    constexpr int LPR = D / (16 / sizeof(T));
+    constexpr int RPB = 256 / LPR;
+    const long long blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const T*>(p.o), reinterpret_cast<const T*>(p.dout), p.dvec, rows);
+  }
+  BwdArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.dout = p.dout; a.lse = p.lse;
+  a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.dvec = p.dvec;
+  a.N = p.N;
+  a.scale = p.scale;
+  a.c = p.scale * kLog2e;
+  a.nblk = (p.N + kBwdOwn - 1) / kBwdOwn;
+  a.total = a.nblk * p.B * p.H;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_bwd_t<T, 64, true>(p, s) : launch_bwd_t<T, 64, false>(p, s);
+  return p.causal ? launch_bwd_t<T, 128, true>(p, s) : launch_bwd_t<T, 128, false>(p, s);
+}
+
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t s) {
+  switch (p.dtype) {
+    case 0: return launch_bwd_d<float>(p, s);
+    case 1: return launch_bwd_d<_Float16>(p, s);
+    default: return launch_bwd_d<__bf16>(p, s);
+  }
+}
+
+}  // namespace fa

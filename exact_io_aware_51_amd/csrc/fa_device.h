@@ -1,0 +1,191 @@
+// fa_device.h -- device-side building blocks for the gfx950 attention kernels.
+//
+// Matrix-core conventions (CDNA4, wave64), checked lane by lane on gfx950:
+//   v_mfma_f32_32x32x16_{bf16,f16}: C[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l%32][8*(l/32) + e], e = 0..7
+//     B: lane l holds B[8*(l/32) + e][l%32]
+//     C: lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l%32]
+//   v_mfma_f32_32x32x2_f32: the same with one element per lane (k = l/32).
+// So a 32x32 accumulator gives each lane one column j = l%32 and 16 rows.
+// Every kernel here computes products with that column standing for the
+// query (or key) the lane owns, so row reductions stay inside a lane plus
+// one swap between the two half-waves.
+//
+// The contraction index of a second product can be permuted freely as long
+// as both operands use the same permutation.  Feeding a 32x32 accumulator
+// (converted to the I/O type) straight in as the B operand uses the
+// permutation "logical k = 8h + e  <->  physical index 8*(r/4) + 4h + r%4"
+// (r = 8t + e for k-step t), which the transposed A operand then reads with
+// ds_read_b64_tr_b16.  Semantics of that instruction on gfx950, per group of
+// 16 lanes: if lane j's address points at four 16-bit values M[j][0..3], lane
+// i receives M[4e + i/4][i%4] in element e.  Pointing lane j at row
+// (base + j/4), columns (c0 + 4*(j%4) .. +3) therefore hands lane i the four
+// rows base..base+3 of column c0 + i: a 4x16 transpose for free.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running-max floor: finite, so that exp2(m_old - m_new) never sees inf - inf.
+constexpr float kMaxFloor = -1.0e30f;
+
+// ---------------------------------------------------------------------------
+// Matrix-core traits per element type.  KS = contraction elements per MFMA;
+// each lane supplies KS/2 consecutive contraction elements.
+template <typename T> struct Mma;
+
+template <> struct Mma<__bf16> {
+  static constexpr int KS = 16;
+  using Frag = bf16x8;
+  __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<_Float16> {
+  static constexpr int KS = 16;
+  using Frag = f16x8;
+  __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 2;
+  using Frag = float;
+  __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fragment loads.
+
+// "Row" fragment: the KS/2 contraction elements lane l supplies, taken from a
+// row stored contiguously (global or LDS).  p points at element (row, k0) of
+// the lane's own row; the lane's half h = l/32 selects the sub-chunk.
+template <typename T>
+__device__ inline typename Mma<T>::Frag row_frag(const T* p, int h) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 raw = *reinterpret_cast<const u32x4*>(p + 8 * h);
+    return __builtin_bit_cast(typename Mma<T>::Frag, raw);
+  } else {
+    return p[h];
+  }
+}
+
+template <typename T>
+__device__ inline typename Mma<T>::Frag zero_frag() {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(typename Mma<T>::Frag, z);
+  } else {
+    return 0.0f;
+  }
+}
+
+template <typename T>
+__device__ inline typename Mma<T>::Frag neg_frag(typename Mma<T>::Frag f) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 raw = __builtin_bit_cast(u32x4, f);
+    raw ^= 0x80008000u;  // exact sign flip of every 16-bit element
+    return __builtin_bit_cast(typename Mma<T>::Frag, raw);
+  } else {
+    return -f;
+  }
+}
+
+// Transposed A fragment for a product whose contraction runs over the rows of
+// a row-major LDS tile (V in P*V, dO in dO^T*P, Q in Q^T*dS, K in K^T*dS).
+//   tile    : LDS tile base, row stride `stride` elements
+//   row0    : first row of the 32-row block being contracted
+//   t       : k-step inside the block (16-bit: 0..1, fp32: 0..15)
+//   col0    : first column of the 32-column output block (M index)
+// Row order follows the accumulator permutation described at the top.
+template <typename T>
+__device__ inline typename Mma<T>::Frag trans_frag(const T* tile, int stride, int row0, int t,
+                                                   int col0, int lane) {
+  const int h = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+    const int i = lane & 15;
+    const int cb = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+    const int rb = row0 + 16 * t + 4 * h + (i >> 2);
+    const T* p0 = tile + rb * stride + cb;
+    const T* p1 = p0 + 8 * stride;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(typename Mma<T>::Frag, both);
+  } else {
+    const int row = row0 + 8 * (t >> 2) + 4 * h + (t & 3);
+    return tile[row * stride + col0 + (lane & 31)];
+  }
+}
+
+// B fragment from a 32x32 fp32 accumulator (k-step t), rounded to T.
+template <typename T>
+__device__ inline typename Mma<T>::Frag acc_frag(const f32x16& c, int t) {
+  if constexpr (sizeof(T) == 2) {
+    typename Mma<T>::Frag f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (T)c[8 * t + e];
+    return f;
+  } else {
+    return c[t];
+  }
+}
+
+// Row (within a 32-row accumulator block) held in register r by half h.
+__device__ constexpr inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Combine a value with its copy in lane l ^ 32 (the other half-wave) without
+// touching LDS.  v_permlane32_swap exchanges one half of each operand with the
+// other, so of the two results one is x and the other is the partner's x;
+// max and sum of the pair are therefore the same in every lane.
+__device__ inline float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Blocks are dispatched round-robin over the 8 XCDs (blockIdx % 8 = XCD).
+// Renumber them so that consecutive logical indices share an XCD (and so its
+// L2): XCD x receives logical blocks [x*q + min(x, r), ...) in order.
+__device__ inline int xcd_remap(int bid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = bid & 7, local = bid >> 3;
+  return x * q + (x < r ? x : r) + local;
+}
+
+// Store 4 consecutive elements (fp32 in) as T.
+template <typename T>
+__device__ inline void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    T4 v = {(T)a, (T)b, (T)c, (T)d};
+    *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,41 @@
+// fa_launch.h -- internal interface between the C ABI and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
+};
+
+struct BwdProblem {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;  // workspace: fp32 [B*H*N] row sums D_i
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;
+};
+
+hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
+hipError_t launch_bwd(const BwdProblem& p, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,111 @@
+/*
+ * fa.h -- C ABI of libfa: fused, tiled exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is exact attention, O = softmax(scale * Q K^T [+ causal mask]) V
+ * ("How Flash Attention Works: Tiling, Softmax, GPU I/O", section "How Flash
+ * Attention Works: The Exact-Attention Idea"; the same formula with scale =
+ * 1/sqrt(d_k) in "attn-flash-equivalence", section "Standard attention I/O is
+ * the bottleneck").  The forward pass never writes the N x N score matrix to
+ * device memory: it keeps a running row max and normaliser per query row and
+ * rescales the partial output as key/value tiles stream past ("How Flash
+ * Attention Works", sections "Tiling Q, K, and V for Fast On-Chip Memory" and
+ * "Online Softmax Without the Full Score Matrix").  Its only side output is one
+ * log-sum-exp per row, from which the backward pass recomputes the score tiles
+ * (same page, section "The Backward Pass: Recomputation Instead of Stored
+ * Activations").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors q, k, v, o, dout, dq, dk, dv are device pointers to contiguous
+ *    [B, H, N, d] arrays, row-major with d fastest, all of one element type
+ *    (fa_dtype).  Offsets are computed in 64-bit.
+ *  - lse is a device pointer to a contiguous fp32 [B, H, N] array holding
+ *    LSE_i = ln sum_j exp(scale * q_i . k_j) over the keys row i may see.
+ *  - Causal mask: query i sees key j iff j <= i (causal = 1); causal = 0 sees all.
+ *  - Supported: d in {64, 128}; N >= 1; B, H >= 1; B*H*N < 2^31; scale finite.
+ *    Anything else returns an error; there is no slower fallback path.
+ *  - Every pointer must be 16-byte aligned.  Outputs must not alias inputs.
+ *  - The caller owns every buffer and keeps it alive until the work queued on
+ *    `stream` has finished.  The library allocates, frees and caches no device
+ *    memory and holds no mutable global state; calls are reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is queued asynchronously; the library never synchronises.
+ *  - Return value: FA_OK or a negative fa_status.  Arguments are validated
+ *    before any HIP call, so an invalid call queues nothing.  A launch failure
+ *    is reported as FA_ERR_HIP; faults during execution surface at the caller's
+ *    next synchronisation.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* NULL/misaligned pointer, bad size, non-finite scale, causal not 0/1 */
+  FA_ERR_UNSUPPORTED = -2, /* a head dimension or dtype this library has no kernel for */
+  FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
+  FA_ERR_HIP = -4          /* the HIP runtime refused a launch (no device, bad stream, ...) */
+} fa_status;
+
+/*
+ * Forward pass.  Writes o = softmax(scale * q k^T [+ mask]) v and, if lse is
+ * not NULL, the per-row log-sum-exp.  Query blocks stream all (or, causal,
+ * all earlier) key/value tiles through on-chip memory; only o and lse reach
+ * device memory ("How Flash Attention Works", section "Kernel Fusion and
+ * Incremental Output Accumulation").
+ *   q, k, v : [B,H,N,d] inputs, dtype `dtype`
+ *   o       : [B,H,N,d] output, dtype `dtype` (rounded to nearest even)
+ *   lse     : [B,H,N] fp32 output, or NULL to skip it (inference)
+ * 16-bit dtypes multiply in the matrix cores with fp32 accumulation; the
+ * softmax weights are rounded to `dtype` before they multiply v.  FA_F32
+ * computes in fp32 throughout.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int N, int d, float scale, int causal,
+           fa_dtype dtype, void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes (fp32 per-row
+ * D_i = sum_c dout_ic * o_ic).  Returns 0 for sizes fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype);
+
+/*
+ * Backward pass: gradients of L = sum(dout * o) with respect to q, k and v.
+ * o and lse must come from fa_fwd with the same q, k, v, scale and causal
+ * (a contract, not checked).  Score tiles are recomputed from q, k and lse,
+ * tile by tile; no probability matrix is read or written ("How Flash Attention
+ * Works", section "The Backward Pass: Recomputation Instead of Stored
+ * Activations").  The gradient formulas are the chain rule on the forward
+ * definition:  dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+ * dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   dq, dk, dv : [B,H,N,d] outputs, dtype `dtype`
+ *   workspace  : device buffer of at least fa_bwd_workspace_bytes() bytes,
+ *                contents on entry ignored, clobbered on exit
+ * The result is deterministic: no atomics, fixed summation order.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *lse,
+           void *dq, void *dk, void *dv,
+           void *workspace, size_t workspace_bytes,
+           int B, int H, int N, int d, float scale, int causal,
+           fa_dtype dtype, void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fa_status_string(int status);
+
+/* Library version as an integer: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

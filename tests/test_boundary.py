@@ -1,0 +1,142 @@
+"""The C-ABI boundary on the CPU: libfa.so loads, exports what include/fa.h
+declares, and rejects every invalid call before any HIP call.
+
+Calls here use made-up (but aligned, non-overlapping) addresses, so they must
+never reach a kernel on a machine that has a GPU: every call that could pass
+validation is skipped unless the machine has no GPU at all.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _no_gpu_here():
+    if os.path.exists("/dev/kfd"):
+        return False
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_io_aware_51_amd as m
+    m.load()
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol(fa):
+    lib = ctypes.CDLL(fa.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), f"libfa.so does not export {name}"
+
+
+def test_status_strings(fa):
+    for st in (0, -1, -2, -3, -4):
+        s = fa.fa_status_string(st)
+        assert s and s != "unknown status"
+    assert fa.fa_status_string(12345) == "unknown status"
+    assert fa.fa_version() == 10000
+
+
+def test_workspace_bytes(fa):
+    assert fa.fa_bwd_workspace_bytes(2, 16, 4096, 128, fa.FA_BF16) == 2 * 16 * 4096 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64, fa.FA_F32) == 256          # rounded up to 256 B
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 96, fa.FA_F16) == 0            # unsupported d
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 64, fa.FA_F16) == 0            # bad size
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 64, 7) == 0                    # bad dtype
+
+
+# Fake, 16-byte aligned, widely spaced addresses (never dereferenced).
+BASE = 1 << 40
+SPAN = 1 << 34
+
+
+def _ptr(i, off=0):
+    return BASE + i * SPAN + off
+
+
+def _fwd(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, N=256, d=64,
+             scale=0.125, causal=0, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                     a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def _bwd(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), dout=_ptr(4), lse=_ptr(5), dq=_ptr(6),
+             dk=_ptr(7), dv=_ptr(8), ws=_ptr(9), wsb=1 << 20, B=1, H=2, N=256, d=64, scale=0.125,
+             causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     a["ws"], a["wsb"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                     a["dtype"], a["stream"])
+
+
+FWD_BAD = [
+    ("null q", dict(q=None), -1), ("null o", dict(o=None), -1),
+    ("misaligned k", dict(k=_ptr(1, 8)), -1), ("misaligned o", dict(o=_ptr(3, 2)), -1),
+    ("misaligned lse", dict(lse=_ptr(4, 2)), -1),
+    ("B=0", dict(B=0), -1), ("H<0", dict(H=-1), -1), ("N=0", dict(N=0), -1), ("d=0", dict(d=0), -1),
+    ("huge B*H*N", dict(B=1 << 16, H=1 << 10, N=1 << 10), -1),
+    ("d=96", dict(d=96), -2), ("d=256", dict(d=256), -2), ("dtype 5", dict(dtype=5), -2),
+    ("nan scale", dict(scale=float("nan")), -1), ("inf scale", dict(scale=float("inf")), -1),
+    ("scale overflows log2e", dict(scale=3.0e38), -1),
+    ("causal 2", dict(causal=2), -1),
+    ("o aliases q", dict(o=_ptr(0)), -1), ("o overlaps v", dict(o=_ptr(2, 4096)), -1),
+    ("lse aliases k", dict(lse=_ptr(1)), -1), ("lse inside o", dict(lse=_ptr(3, 64)), -1),
+]
+
+BWD_BAD = [
+    ("null dout", dict(dout=None), -1), ("null lse", dict(lse=None), -1), ("null dv", dict(dv=None), -1),
+    ("misaligned dq", dict(dq=_ptr(6, 4)), -1), ("misaligned lse", dict(lse=_ptr(5, 1)), -1),
+    ("d=32", dict(d=32), -2), ("N=0", dict(N=0), -1), ("causal -1", dict(causal=-1), -1),
+    ("no workspace", dict(ws=None), -3), ("small workspace", dict(wsb=100), -3),
+    ("misaligned workspace", dict(ws=_ptr(9, 4)), -3),
+    ("workspace overlaps dk", dict(ws=_ptr(7, 16)), -3), ("workspace overlaps q", dict(ws=_ptr(0)), -3),
+    ("dq aliases dk", dict(dk=_ptr(6)), -1), ("dv aliases v", dict(dv=_ptr(2)), -1),
+    ("dq aliases lse", dict(dq=_ptr(5)), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", FWD_BAD, ids=[x[0] for x in FWD_BAD])
+def test_fwd_rejects(fa, name, kw, want):
+    assert _fwd(fa, **kw) == want
+
+
+@pytest.mark.parametrize("name,kw,want", BWD_BAD, ids=[x[0] for x in BWD_BAD])
+def test_bwd_rejects(fa, name, kw, want):
+    assert _bwd(fa, **kw) == want
+
+
+@pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
+def test_valid_call_without_device_reports_hip_error(fa):
+    assert _fwd(fa) == fa.FA_ERR_HIP
+    assert _fwd(fa, lse=None, causal=1, dtype=fa.FA_F32, scale=-1.0) == fa.FA_ERR_HIP
+    assert _bwd(fa) == fa.FA_ERR_HIP
+
+
+def test_python_helpers_refuse_cpu_tensors(fa):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, torch.zeros(1, 1, 4), q)
+    assert math.isclose(1 / math.sqrt(64), 0.125)

@@ -1,0 +1,137 @@
+"""Forward parity: the HIP path through the C ABI against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_51_amd import workloads as W
+from gates import check, check_lse, to_np
+from gpu_util import announce, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _fwd(q, k, v, scale, causal, **kw):
+    import exact_io_aware_51_amd as fa
+    o, lse = fa.forward(q, k, v, scale=scale, causal=causal, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------- small shapes
+SHAPES = [(1, 2, n, d) for n in (1, 2, 7, 63, 65, 100, 127, 129, 257, 1000) for d in (64, 128)]
+SHAPES += [(2, 3, 191, 64), (3, 1, 300, 128)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_small_shapes(shape, causal, dtype):
+    dev = device()
+    B, H, N, d = shape
+    w = W.shape_case(B, H, N, d, dtype, causal, seed=17 + N + d, mode="fwd")
+    announce("fwd", w.name)
+    q, k, v = W.make_inputs(w)
+    o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, causal)
+    ro, rl = oracle.attention_forward(q, k, v, w.scale, causal)
+    check(o, ro, dtype, f"O {w.name}")
+    check_lse(lse, rl, dtype, f"LSE {w.name}")
+
+
+# ------------------------------------------------------- the five workloads
+def _sample_rows(N, rng, n=48):
+    rows = {0, 1, N // 2, N - 2, N - 1}
+    rows.update(rng.choice(N, size=min(N, n), replace=False).tolist())
+    return sorted(r for r in rows if 0 <= r < N)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_fwd_workloads(name):
+    """Full-size launch; rows of a few heads checked against the oracle one by one."""
+    dev = device()
+    w = W.WORKLOADS[name]
+    announce("fwd workload", name)
+    q, k, v = W.make_inputs(w, with_grad=False)
+    o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, w.causal)
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert torch.isfinite(o_c.float()).all() and torch.isfinite(lse_c).all()
+    if w.N * w.B * w.H <= 4096:
+        ro, rl = oracle.attention_forward(q, k, v, w.scale, w.causal)
+        check(o_c, ro, w.dtype, f"O {name}")
+        check_lse(lse_c, rl, w.dtype, f"LSE {name}")
+        return
+    rng = np.random.default_rng(5)
+    heads = {(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
+    got, ref, gl, rlse = [], [], [], []
+    for (b, h) in sorted(heads):
+        rows = _sample_rows(w.N, rng)
+        so, sl = oracle.attention_forward_rows(q, k, v, w.scale, w.causal, b, h, rows)
+        got.append(to_np(o_c[b, h, rows]))
+        ref.append(so)
+        gl.append(to_np(lse_c[b, h, rows]))
+        rlse.append(sl)
+    check(np.concatenate(got), np.concatenate(ref), w.dtype, f"O rows {name}")
+    check_lse(np.concatenate(gl), np.concatenate(rlse), w.dtype, f"LSE rows {name}")
+
+
+# ----------------------------------------------------------- special cases
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fwd_causal_row0_is_v0_exactly(dtype):
+    dev = device()
+    w = W.shape_case(2, 2, 333, 128, dtype, True, seed=5, mode="fwd")
+    announce("fwd row0", w.name)
+    q, k, v = W.make_inputs(w)
+    o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, True)
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0]), "causal row 0 must equal V_0 exactly"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_q_zero_gives_means(causal):
+    """Q = 0: uniform weights over the visible keys, LSE = ln(count)."""
+    dev = device()
+    w = W.shape_case(1, 2, 517, 64, "bf16", causal, seed=6, mode="fwd")
+    announce("fwd q=0", w.name)
+    _, k, v = W.make_inputs(w)
+    q = torch.zeros_like(k)
+    o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, causal)
+    vv = to_np(v)
+    cnt = np.arange(1, 518, dtype=np.float64) if causal else np.full(517, 517.0)
+    ref = np.cumsum(vv, axis=2) / cnt[:, None] if causal else np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+    check(o, ref, "bf16", "Q=0 means")
+    check_lse(lse, np.broadcast_to(np.log(cnt), (1, 2, 517)), "bf16", "Q=0 LSE")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+def test_fwd_unusual_scales(scale):
+    dev = device()
+    w = W.shape_case(1, 2, 200, 64, "bf16", True, seed=7, mode="fwd")
+    announce("fwd scale", scale)
+    q, k, v = W.make_inputs(w)
+    o, lse = _fwd(*to_dev((q, k, v), dev), scale, True)
+    ro, rl = oracle.attention_forward(q, k, v, np.float32(scale), True)
+    check(o, ro, "bf16", f"O scale={scale}")
+    check_lse(lse, rl, "bf16", f"LSE scale={scale}")
+
+
+def test_fwd_peaked_scores_are_stable():
+    """Large scores (peaked softmax rows) exercise the running-max rescaling."""
+    dev = device()
+    w = W.shape_case(1, 2, 700, 128, "bf16", False, seed=8, mode="fwd", q_scale=4.0)
+    announce("fwd peaked", w.name)
+    q, k, v = W.make_inputs(w)
+    o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, False)
+    ro, rl = oracle.attention_forward(q, k, v, w.scale, False)
+    check(o, ro, "bf16", "O peaked")
+    assert np.max(np.abs(to_np(lse) - rl)) < 5e-3
+
+
+def test_fwd_without_lse_and_determinism():
+    dev = device()
+    w = W.shape_case(2, 4, 1031, 128, "bf16", True, seed=9, mode="fwd")
+    announce("fwd determinism", w.name)
+    q, k, v = to_dev(W.make_inputs(w), dev)
+    o1, l1 = _fwd(q, k, v, w.scale, True)
+    o2, l2 = _fwd(q, k, v, w.scale, True)
+    o3, l3 = _fwd(q, k, v, w.scale, True, need_lse=False)
+    assert l3 is None
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1, o3)
