@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Throughput of the fused exact-attention hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic input: the forward kernel
+(O, LSE) followed by the three backward stages (row sums D, dK/dV, dQ) of the
+fwd+bwd workload c5 (bf16, B=2, H=16, N=4096, d=128, causal).  Inputs are
+resident in device memory before the timed region starts.  Each kernel is
+bracketed by HIP events on the stream it is launched on, so the per-kernel
+averages (and the roofline of the dominant kernel) are measured live.
+
+Prints ONE JSON line on stdout.  Everything else goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (fwd, fwd+bwd; causal-adjusted) and % of MI355X bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_io_aware_51_amd/csrc/fa_fwd.hip", "exact_io_aware_51_amd/csrc/fa_bwd.hip",
+                  "exact_io_aware_51_amd/csrc/fa_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_models(w):
+    """Algorithmic flops and bytes per launch of each kernel of one step.
+
+    Flops count only the products the method needs (forward: S and PV; backward:
+    the S recompute, dV, dP, dQ, dK), halved under the causal mask.  The dQ
+    kernel also recomputes S and dP, which is extra work and not counted.
+    Bytes count each input read once and each output written once.
+    """
+    e = 2 if w.dtype in ("bf16", "f16") else 4
+    bh, n, d = w.B * w.H, w.N, w.d
+    half = 0.5 if w.causal else 1.0
+    nn = float(n) * n * d * bh * half
+    t = float(n) * d * e * bh   # one [B,H,N,d] tensor
+    r = 4.0 * n * bh            # one fp32 [B,H,N] vector
+    return {
+        "fwd": {"flops": 4 * nn, "bytes": 3 * t + t + r},
+        "bwd_rowsum": {"flops": 2.0 * n * d * bh, "bytes": 2 * t + r},
+        "bwd_dkdv": {"flops": 8 * nn, "bytes": 4 * t + 2 * r + 2 * t},
+        "bwd_dq": {"flops": 2 * nn, "bytes": 4 * t + 2 * r + t},
+    }
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from committed counter runs, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("kernels", {}).get(kernel)
+    if not entry or t.get("source_digest") != source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle on whole heads of the same workload until `seconds` have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from exact_io_aware_51_amd import workloads as W
+    q, k, v, do = W.make_inputs(w)
+    models = kernel_models(w)
+    per_head = sum(m["flops"] for m in models.values()) / (w.B * w.H)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t0 = 0, time.perf_counter()
+    for (b, h) in heads:
+        sl = slice(b, b + 1), slice(h, h + 1)
+        oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal)
+        oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": per_head * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of workload {w.name} (fwd+bwd per head, fp64 numpy, "
+                      f"{dt:.1f} s; algorithmic causal-adjusted flops)"}
+
+
+class Runner:
+    """Device buffers and raw C-ABI calls for one workload."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        import exact_io_aware_51_amd as fa
+        from exact_io_aware_51_amd import workloads as W
+        self.fa, self.w = fa, w
+        with_grad = w.mode == "fwd+bwd"
+        ins = [t.to(dev) for t in W.make_inputs(w, with_grad=with_grad)]
+        self.q, self.k, self.v = ins[:3]
+        self.do = ins[3] if with_grad else None
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        self.code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16}[w.dtype]
+        if with_grad:
+            self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+            self.wsb = fa.fa_bwd_workspace_bytes(w.B, w.H, w.N, w.d, self.code)
+            self.ws = torch.empty(self.wsb, dtype=torch.uint8, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        self.dims = (w.B, w.H, w.N, w.d)
+
+    def _ok(self, st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {self.fa.fa_status_string(st)}")
+
+    def fwd(self):
+        w = self.w
+        self._ok(self.fa.fa_fwd(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                                self.lse.data_ptr(), *self.dims, w.scale, int(w.causal), self.code, self.stream),
+                 "fa_fwd")
+
+    def rowsum(self):
+        self._ok(self.fa.fa_bwd_rowsum(self.o.data_ptr(), self.do.data_ptr(), self.ws.data_ptr(), self.wsb,
+                                       *self.dims, self.code, self.stream), "fa_bwd_rowsum")
+
+    def dkdv(self):
+        w = self.w
+        self._ok(self.fa.fa_bwd_dkdv(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.do.data_ptr(),
+                                     self.lse.data_ptr(), self.ws.data_ptr(), self.wsb, self.dk.data_ptr(),
+                                     self.dv.data_ptr(), *self.dims, w.scale, int(w.causal), self.code,
+                                     self.stream), "fa_bwd_dkdv")
+
+    def dq_(self):
+        w = self.w
+        self._ok(self.fa.fa_bwd_dq(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.do.data_ptr(),
+                                   self.lse.data_ptr(), self.ws.data_ptr(), self.wsb, self.dq.data_ptr(),
+                                   *self.dims, w.scale, int(w.causal), self.code, self.stream), "fa_bwd_dq")
+
+
+def time_fwd_only(name, dev, iters=20, warmup=3):
+    import torch
+
+    from exact_io_aware_51_amd import workloads as W
+    w = W.WORKLOADS[name]
+    r = Runner(w, dev)
+    for _ in range(warmup):
+        r.fwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        ev[2 * i].record()
+        r.fwd()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)) / iters
+    tf = w.fwd_flops() / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+            "shape": f"{w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5", help="fwd+bwd workload timed as the step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-fwd-workloads", action="store_true", help="skip the forward-only lines for c1..c4")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the attention path shards (batch, head) pairs across GPUs with no communication, "
+              "so there is no multi-GPU step to time here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_io_aware_51_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    if w.mode != "fwd+bwd":
+        raise SystemExit(f"workload {w.name} has no backward; the step needs fwd+bwd")
+    log(f"bench: workload {w.name} {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+    r = Runner(w, dev)
+    stages = [("fwd", r.fwd), ("bwd_rowsum", r.rowsum), ("bwd_dkdv", r.dkdv), ("bwd_dq", r.dq_)]
+
+    for _ in range(args.warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record()
+        for i, (_, f) in enumerate(stages):
+            f()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    models = kernel_models(w)
+    step_flops = sum(m["flops"] for m in models.values())
+    kernels = {}
+    for i, (name, _) in enumerate(stages):
+        ms = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
+        m = models[name]
+        kernels[name] = {"ms": round(ms, 4), "tflops": round(m["flops"] / (ms * 1e-3) / 1e12, 1),
+                         "gbs": round(m["bytes"] / (ms * 1e-3) / 1e9, 1)}
+    event_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(K)) / K
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dm = models[dom]
+    dom_ms = kernels[dom]["ms"]
+    mfma_bound = dm["flops"] / dm["bytes"] > PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        ach = dm["flops"] / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_TFLOPS[w.dtype], 4)}
+    else:
+        ach = dm["bytes"] / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = traffic_for(dom)
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = {"flops": dm["flops"], "bytes": dm["bytes"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_flops * K / wall / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: fwd+bwd, {w.dtype}, B={w.B} H={w.H} N={w.N} d={w.d}, "
+                               f"{'causal' if w.causal else 'non-causal'}, seeded N(0,1) Q/K/V/dO",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "parallelism": "single GPU; (batch, head) pairs would shard across GPUs"},
+        "frac_of_peak": round(step_flops * K / wall / 1e12 / PEAK_TFLOPS[w.dtype], 4),
+        "event_ms_per_step": round(event_ms, 4),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_fwd_workloads:
+        fw = {}
+        for name in ("c1", "c2", "c3", "c4"):
+            log(f"bench: forward-only {name}")
+            fw[name] = time_fwd_only(name, dev)
+        fw["c5"] = {"ms": kernels["fwd"]["ms"], "tflops": kernels["fwd"]["tflops"],
+                    "frac_of_peak": round(kernels["fwd"]["tflops"] / PEAK_TFLOPS[w.dtype], 4)}
+        out["fwd_workloads"] = fw
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

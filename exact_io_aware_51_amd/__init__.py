@@ -15,7 +15,8 @@ import math
 import os
 
 __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_status_string", "fa_version", "forward", "backward", "library_path", "load"]
+           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_status_string", "fa_version",
+           "forward", "backward", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
@@ -23,7 +24,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0,
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_version")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
+           "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -51,6 +53,12 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_rowsum.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+    lib.fa_bwd_rowsum.restype = i
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_dkdv.restype = i
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_dq.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -70,6 +78,22 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, 
            dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                          scale, causal, dtype, stream)
+
+
+def fa_bwd_rowsum(o, dout, workspace, workspace_bytes, B, H, N, d, dtype, stream) -> int:
+    return load().fa_bwd_rowsum(o, dout, workspace, workspace_bytes, B, H, N, d, dtype, stream)
+
+
+def fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, B, H, N, d, scale, causal,
+                dtype, stream) -> int:
+    return load().fa_bwd_dkdv(q, k, v, dout, lse, workspace, workspace_bytes, dk, dv, B, H, N, d, scale,
+                              causal, dtype, stream)
+
+
+def fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, scale, causal, dtype,
+              stream) -> int:
+    return load().fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, scale, causal,
+                            dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:

@@ -88,36 +88,106 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
   return (need + 255) & ~(size_t)255;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation of a backward call (or one stage of it).  A slot the stage does
+// not use holds kUnused (the address of a private host object, which no caller
+// can pass by accident); every other pointer is checked.
+struct BwdPtrs {
+  const void *q, *k, *v, *o, *dout, *lse;
+  void *dq, *dk, *dv, *ws;
+};
+
+const char kUnusedTag = 0;
+const void* const kUnused = &kUnusedTag;
+
+int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+              int dtype) {
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const void* p16[] = {p.q, p.k, p.v, p.o, p.dout, p.dq, p.dk, p.dv};
+  for (const void* x : p16) {
+    if (x == kUnused) continue;
+    if (!x || !aligned(x, 16)) return FA_ERR_INVALID_ARG;
+  }
+  if (p.lse != kUnused && (!p.lse || !aligned(p.lse, 4))) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, (fa_dtype)dtype);
+  if (!p.ws || workspace_bytes < need || !aligned(p.ws, 16)) return FA_ERR_WORKSPACE;
+  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const Range ins[6] = {{p.q, tb}, {p.k, tb}, {p.v, tb}, {p.o, tb}, {p.dout, tb}, {p.lse, lb}};
+  const Range outs[4] = {{p.dq, tb}, {p.dk, tb}, {p.dv, tb}, {p.ws, need}};
+  for (int i = 0; i < 4; ++i) {
+    if (outs[i].p == kUnused) continue;
+    for (const Range& r : ins)
+      if (r.p != kUnused && overlap(outs[i], r)) return i == 3 ? FA_ERR_WORKSPACE : FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (outs[j].p != kUnused && overlap(outs[i], outs[j])) return j == 3 ? FA_ERR_WORKSPACE : FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int N, int d, float scale, int causal, int dtype) {
+  fa::BwdProblem b;
+  auto use = [](const void* x) { return x == kUnused ? nullptr : x; };
+  b.q = use(p.q); b.k = use(p.k); b.v = use(p.v); b.o = use(p.o); b.dout = use(p.dout);
+  b.lse = static_cast<const float*>(use(p.lse));
+  b.dq = const_cast<void*>(use(p.dq)); b.dk = const_cast<void*>(use(p.dk)); b.dv = const_cast<void*>(use(p.dv));
+  b.dvec = static_cast<float*>(p.ws);
+  b.B = B; b.H = H; b.N = N; b.d = d;
+  b.scale = scale; b.causal = causal; b.dtype = dtype;
+  return b;
+}
+
+int run_stages(const fa::BwdProblem& b, int first, int last, void* stream) {
+  (void)hipGetLastError();  // report only these launches' errors
+  hipError_t e = hipSuccess;
+  for (int s = first; s <= last && e == hipSuccess; ++s) e = fa::launch_bwd_stage(b, s, reinterpret_cast<hipStream_t>(stream));
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, fa_dtype dtype, void* stream) {
-  int st = check_common(B, H, N, d, scale, causal, (int)dtype);
+  const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  int st = check_bwd(p, workspace_bytes, B, H, N, d, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-  const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
-  for (const void* p : p16)
-    if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
-  if (!aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
-  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
-  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const Range ins[6] = {{q, tb}, {k, tb}, {v, tb}, {o, tb}, {dout, tb}, {lse, lb}};
-  const Range outs[4] = {{dq, tb}, {dk, tb}, {dv, tb}, {workspace, need}};
-  for (int i = 0; i < 4; ++i) {
-    for (const Range& r : ins)
-      if (overlap(outs[i], r)) return i == 3 ? FA_ERR_WORKSPACE : FA_ERR_INVALID_ARG;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return j == 3 ? FA_ERR_WORKSPACE : FA_ERR_INVALID_ARG;
-  }
+  return run_stages(bwd_problem(p, B, H, N, d, scale, causal, (int)dtype), 0, 2, stream);
+}
 
-  fa::BwdProblem p;
-  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
-  p.dq = dq; p.dk = dk; p.dv = dv; p.dvec = static_cast<float*>(workspace);
-  p.B = B; p.H = H; p.N = N; p.d = d;
-  p.scale = scale; p.causal = causal; p.dtype = (int)dtype;
-  (void)hipGetLastError();
-  return hip_status(fa::launch_bwd(p, reinterpret_cast<hipStream_t>(stream)));
+int fa_bwd_rowsum(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B, int H, int N,
+                  int d, fa_dtype dtype, void* stream) {
+  void* un = const_cast<void*>(kUnused);
+  const BwdPtrs p{kUnused, kUnused, kUnused, o, dout, kUnused, un, un, un, workspace};
+  int st = check_bwd(p, workspace_bytes, B, H, N, d, 1.0f, 0, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, N, d, 1.0f, 0, (int)dtype), 0, 0, stream);
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d,
+                float scale, int causal, fa_dtype dtype, void* stream) {
+  void* un = const_cast<void*>(kUnused);
+  const BwdPtrs p{q, k, v, kUnused, dout, lse, un, dk, dv, const_cast<void*>(workspace)};
+  int st = check_bwd(p, workspace_bytes, B, H, N, d, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, N, d, scale, causal, (int)dtype), 1, 1, stream);
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, const void* workspace,
+              size_t workspace_bytes, void* dq, int B, int H, int N, int d, float scale, int causal, fa_dtype dtype,
+              void* stream) {
+  void* un = const_cast<void*>(kUnused);
+  const BwdPtrs p{q, k, v, kUnused, dout, lse, dq, un, un, const_cast<void*>(workspace)};
+  int st = check_bwd(p, workspace_bytes, B, H, N, d, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, N, d, scale, causal, (int)dtype), 2, 2, stream);
 }
 
 }  // extern "C"

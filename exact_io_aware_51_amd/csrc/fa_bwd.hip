@@ -404,14 +404,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
 // --------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
-  const long long rows = (long long)p.B * p.H * p.N;
-  {
+static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t stream) {
+  if (stage == 0) {
+    const long long rows = (long long)p.B * p.H * p.N;
     constexpr int LPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / LPR;
     const long long blocks = (rows + RPB - 1) / RPB;
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const T*>(p.o), reinterpret_cast<const T*>(p.dout), p.dvec, rows);
+    return hipGetLastError();
   }
   BwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.dout = p.dout; a.lse = p.lse;
@@ -421,22 +422,24 @@ static hipError_t launch_bwd_t(const BwdProblem& p, hipStream_t stream) {
   a.c = p.scale * kLog2e;
   a.nblk = (p.N + kBwdOwn - 1) / kBwdOwn;
   a.total = a.nblk * p.B * p.H;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+  if (stage == 1)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_bwd_d(const BwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_bwd_t<T, 64, true>(p, s) : launch_bwd_t<T, 64, false>(p, s);
-  return p.causal ? launch_bwd_t<T, 128, true>(p, s) : launch_bwd_t<T, 128, false>(p, s);
+static hipError_t launch_bwd_d(const BwdProblem& p, int stage, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_bwd_t<T, 64, true>(p, stage, s) : launch_bwd_t<T, 64, false>(p, stage, s);
+  return p.causal ? launch_bwd_t<T, 128, true>(p, stage, s) : launch_bwd_t<T, 128, false>(p, stage, s);
 }
 
-hipError_t launch_bwd(const BwdProblem& p, hipStream_t s) {
+hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s) {
   switch (p.dtype) {
-    case 0: return launch_bwd_d<float>(p, s);
-    case 1: return launch_bwd_d<_Float16>(p, s);
-    default: return launch_bwd_d<__bf16>(p, s);
+    case 0: return launch_bwd_d<float>(p, stage, s);
+    case 1: return launch_bwd_d<_Float16>(p, stage, s);
+    default: return launch_bwd_d<__bf16>(p, stage, s);
   }
 }
 

@@ -98,6 +98,27 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            int B, int H, int N, int d, float scale, int causal,
            fa_dtype dtype, void *stream);
 
+/*
+ * The three stages fa_bwd queues, for callers that schedule them themselves
+ * (for instance dK/dV and dQ on two streams once the row sums are done, or
+ * timing each stage).  fa_bwd(...) is exactly
+ *     fa_bwd_rowsum(...); fa_bwd_dkdv(...); fa_bwd_dq(...);
+ * on one stream.  Arguments mean what they mean for fa_bwd; each stage
+ * validates the arguments it uses.  The workspace carries D from
+ * fa_bwd_rowsum to the other two stages, so it must not be reused in between.
+ *   fa_bwd_rowsum : workspace <- D_i = sum_c dout_ic * o_ic (fp32)
+ *   fa_bwd_dkdv   : dk, dv   (reads q, k, v, dout, lse, workspace)
+ *   fa_bwd_dq     : dq       (reads q, k, v, dout, lse, workspace)
+ */
+int fa_bwd_rowsum(const void *o, const void *dout, void *workspace, size_t workspace_bytes,
+                  int B, int H, int N, int d, fa_dtype dtype, void *stream);
+int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+                const void *workspace, size_t workspace_bytes, void *dk, void *dv,
+                int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
+int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+              const void *workspace, size_t workspace_bytes, void *dq,
+              int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -37,7 +37,8 @@ def _declared():
 
 
 def test_header_declares_the_abi():
-    assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_version"])
+    assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv",
+                                  "fa_bwd_dq", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -125,11 +126,31 @@ def test_bwd_rejects(fa, name, kw, want):
     assert _bwd(fa, **kw) == want
 
 
+STAGE_BAD = [
+    ("rowsum null o", lambda fa: fa.fa_bwd_rowsum(None, _ptr(4), _ptr(9), 1 << 20, 1, 2, 256, 64, fa.FA_BF16, None), -1),
+    ("rowsum small ws", lambda fa: fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(9), 64, 1, 2, 256, 64, fa.FA_BF16, None), -3),
+    ("rowsum ws aliases o", lambda fa: fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(3), 1 << 20, 1, 2, 256, 64, fa.FA_BF16, None), -3),
+    ("rowsum d=80", lambda fa: fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(9), 1 << 20, 1, 2, 256, 80, fa.FA_BF16, None), -2),
+    ("dkdv null lse", lambda fa: fa.fa_bwd_dkdv(_ptr(0), _ptr(1), _ptr(2), _ptr(4), None, _ptr(9), 1 << 20, _ptr(7), _ptr(8), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -1),
+    ("dkdv dk aliases dv", lambda fa: fa.fa_bwd_dkdv(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), _ptr(9), 1 << 20, _ptr(7), _ptr(7), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -1),
+    ("dkdv nan scale", lambda fa: fa.fa_bwd_dkdv(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), _ptr(9), 1 << 20, _ptr(7), _ptr(8), 1, 2, 256, 64, float("nan"), 1, fa.FA_BF16, None), -1),
+    ("dq misaligned dq", lambda fa: fa.fa_bwd_dq(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), _ptr(9), 1 << 20, _ptr(6, 8), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -1),
+    ("dq no workspace", lambda fa: fa.fa_bwd_dq(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), None, 1 << 20, _ptr(6), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -3),
+    ("dq aliases k", lambda fa: fa.fa_bwd_dq(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), _ptr(9), 1 << 20, _ptr(1), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -1),
+]
+
+
+@pytest.mark.parametrize("name,call,want", STAGE_BAD, ids=[x[0] for x in STAGE_BAD])
+def test_bwd_stages_reject(fa, name, call, want):
+    assert call(fa) == want
+
+
 @pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
 def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd(fa) == fa.FA_ERR_HIP
     assert _fwd(fa, lse=None, causal=1, dtype=fa.FA_F32, scale=-1.0) == fa.FA_ERR_HIP
     assert _bwd(fa) == fa.FA_ERR_HIP
+    assert fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(9), 1 << 20, 1, 2, 256, 64, fa.FA_BF16, None) == fa.FA_ERR_HIP
 
 
 def test_python_helpers_refuse_cpu_tensors(fa):
