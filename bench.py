@@ -188,6 +188,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-fwd-workloads", action="store_true", help="skip the forward-only lines for c1..c4")
+    ap.add_argument("--fwd-workload", default=None,
+                    help="diagnostic: time only the forward kernel of this workload (c1..c5), one JSON line")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="diagnostic: run a plain device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -204,6 +208,20 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
+        return
+    if args.fwd_workload:
+        res = time_fwd_only(args.fwd_workload, dev, iters=args.steps, warmup=args.warmup)
+        res["workload"] = args.fwd_workload
+        print(json.dumps(res), flush=True)
+        return
     w = W.WORKLOADS[args.workload]
     if w.mode != "fwd+bwd":
         raise SystemExit(f"workload {w.name} has no backward; the step needs fwd+bwd")

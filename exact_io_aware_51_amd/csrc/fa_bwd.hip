@@ -105,8 +105,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int N = a.N;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
-  const int bh = bid / a.nblk;
-  const int kblk = bid - bh * a.nblk;
+  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);  // wave-uniform: keep scalar
+  const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   const int kb0 = kblk * kBwdOwn;
   const int kw = kb0 + 32 * wave;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int N = a.N;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
-  const int bh = bid / a.nblk;
-  int qb = bid - bh * a.nblk;
+  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);  // wave-uniform: keep scalar
+  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   if (CAUSAL) qb = a.nblk - 1 - qb;
   const int q0 = qb * kBwdOwn;
   const int qw = q0 + 32 * wave;

@@ -176,6 +176,19 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// Buffer resource over `bytes` bytes starting at `base`: raw buffer loads at
+// offsets at or beyond `bytes` return zeros, which pads ragged tiles for free.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Wave-uniform "does any lane want this".
+__device__ inline bool any_lane(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
+
 // Store 4 consecutive elements (fp32 in) as T.
 template <typename T>
 __device__ inline void store4(T* p, float a, float b, float c, float d) {

@@ -18,6 +18,8 @@
 //     only diagonal/edge tiles evaluate the mask (FlashAttention-2's trimming of
 //     non-matmul work, same page, section "FlashAttention 1 vs 2 vs 3").
 // Only O and one log-sum-exp per row are written to device memory.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -56,8 +58,14 @@ struct FwdLayout {
   static_assert(kFwdBN * CPR % kFwdThreads == 0, "tile chunks must split evenly");
 };
 
+// Rescale the running output only when some row's max has grown by more than
+// 2^kTau since the reference max was last moved.  O and l are always scaled
+// against the same reference, so the final O = acc / l is unchanged; the
+// weights 2^(c s - m) stay below 2^kTau, far inside fp32 and bf16 range.
+constexpr float kTau = 8.0f;
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) void fwd_kernel(FwdArgs a) {
   using M = Mma<T>;
   using L = FwdLayout<T, D>;
   using Frag = typename M::Frag;
@@ -74,26 +82,26 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
   const int h = lane >> 5, col = lane & 31;
   const int N = a.N;
 
+  // block coordinates are wave-uniform; keep them (and every address built
+  // from them) in scalar registers
   const int bid = xcd_remap(blockIdx.x, a.total);
-  const int bh = bid / a.nqb;
-  int qb = bid - bh * a.nqb;
+  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
+  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
   if (CAUSAL) qb = a.nqb - 1 - qb;  // the longest causal rows start first
   const int q0 = qb * kFwdBM;
   const int qw = q0 + wave * 32;
   const size_t head = (size_t)bh * (size_t)N * D;
   const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
-  const T* __restrict__ K = reinterpret_cast<const T*>(a.k) + head;
-  const T* __restrict__ V = reinterpret_cast<const T*>(a.v) + head;
+  const char* Kb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + head);
+  const char* Vb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + head);
 
   // Q rows of this lane's query column, as B fragments (k = d).
+  const int myq = qw + col;
   Frag qf[KSTEPS];
-  {
-    const int qrow = qw + col;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      qf[ks] = qrow < N ? row_frag<T>(Q + (size_t)qrow * D + ks * M::KS, h) : zero_frag<T>();
-      if (a.negate) qf[ks] = neg_frag<T>(qf[ks]);
-    }
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
+    if (a.negate) qf[ks] = neg_frag<T>(qf[ks]);
   }
 
   const int ntiles_all = (N + kFwdBN - 1) / kFwdBN;
@@ -102,44 +110,110 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     const int last = (q0 + kFwdBM - 1) / kFwdBN + 1;
     ntiles = last < ntiles_all ? last : ntiles_all;
   }
+  // largest key this lane's query may see
+  const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
 
-  // Global -> register staging of one K/V tile (16-byte chunks, coalesced).
+  // Global -> register staging of one K/V tile: 16-byte chunks, coalesced.
+  // The buffer view of the tile ends at key N, so reads past it return zeros.
+  uint32_t goff[L::PER_THREAD], soff[L::PER_THREAD], voff[L::PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < L::PER_THREAD; ++i) {
+    const int c = tid + i * kFwdThreads;
+    const int row = c / L::CPR, cc = c - row * L::CPR;
+    goff[i] = row * L::ROWB + cc * 16;
+    soff[i] = (row * L::KSTR + cc * (16 / sizeof(T))) * sizeof(T);
+    voff[i] = (row * L::VSTR + cc * (16 / sizeof(T))) * sizeof(T);
+  }
   u32x4 kreg[L::PER_THREAD], vreg[L::PER_THREAD];
   auto load_tile = [&](int j) {
-    const int k0 = j * kFwdBN;
+    const uint32_t base = (uint32_t)(j * kFwdBN) * L::ROWB;
+    const uint32_t left = (uint32_t)(N - j * kFwdBN) * L::ROWB;
+    const auto rk = buffer_rsrc(Kb + base, left);
+    const auto rv = buffer_rsrc(Vb + base, left);
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i) {
-      const int c = tid + i * kFwdThreads;
-      const int row = c / L::CPR, cc = c - row * L::CPR;
-      const int key = k0 + row;
-      if (key < N) {
-        const size_t off = (size_t)key * D + cc * (16 / sizeof(T));
-        kreg[i] = *reinterpret_cast<const u32x4*>(K + off);
-        vreg[i] = *reinterpret_cast<const u32x4*>(V + off);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      kreg[i] = buffer_load16(rk, goff[i]);
+      vreg[i] = buffer_load16(rv, goff[i]);
     }
   };
   auto store_tile = [&](int buf) {
+    char* kd = reinterpret_cast<char*>(lds_k + buf * L::KTILE);
+    char* vd = reinterpret_cast<char*>(lds_v + buf * L::VTILE);
 #pragma unroll
     for (int i = 0; i < L::PER_THREAD; ++i) {
-      const int c = tid + i * kFwdThreads;
-      const int row = c / L::CPR, cc = c - row * L::CPR;
-      const int e = cc * (16 / sizeof(T));
-      *reinterpret_cast<u32x4*>(lds_k + buf * L::KTILE + row * L::KSTR + e) = kreg[i];
-      *reinterpret_cast<u32x4*>(lds_v + buf * L::VTILE + row * L::VSTR + e) = vreg[i];
+      *reinterpret_cast<u32x4*>(kd + soff[i]) = kreg[i];
+      *reinterpret_cast<u32x4*>(vd + voff[i]) = vreg[i];
     }
   };
 
   f32x16 oacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
-  float m = kMaxFloor;  // running max of c * s over the keys seen so far (log2 units)
-  float l = 0.0f;       // running normaliser sum 2^(c s - m)
+  float m = kMaxFloor;  // reference max of c * s (log2 units), same in both half-waves
+  float l = 0.0f;       // this half-wave's share of sum 2^(c s - m)
   const float c = a.c;
-  const int myq = qw + col;
+
+  // One 64-key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](const T* kt, const T* vt, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    const T* kr0 = kt + col * L::KSTR;
+    const T* kr1 = kt + (32 + col) * L::KSTR;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      s0 = M::mma(row_frag<T>(kr0 + ks * M::KS, h), qf[ks], s0);
+      s1 = M::mma(row_frag<T>(kr1 + ks * M::KS, h), qf[ks], s1);
+    }
+    // key of register r in block kb is k0 + 32 kb + acc_row(r, h); allowed iff <= lim
+    const int t0 = lim - k0 - 4 * h, t1 = t0 - 32;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ro = 8 * (r >> 2) + (r & 3);
+      float x0 = s0[r], x1 = s1[r];
+      if constexpr (MASK) {
+        x0 = ro <= t0 ? x0 : -__builtin_inff();
+        x1 = ro <= t1 ? x1 : -__builtin_inff();
+      }
+      mx = __builtin_fmaxf(mx, __builtin_fmaxf(x0, x1));
+    }
+    mx = halves_max(mx);
+    float mt = mx * c;
+    if constexpr (MASK) mt = mx > -__builtin_inff() ? mt : -__builtin_inff();
+    if (any_lane(mt > m + kTau)) {
+      const float mnew = __builtin_fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      m = mnew;
+    }
+    const float negm = -m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p0 = fast_exp2(__builtin_fmaf(s0[r], c, negm));
+      float p1 = fast_exp2(__builtin_fmaf(s1[r], c, negm));
+      if constexpr (MASK) {
+        const int ro = 8 * (r >> 2) + (r & 3);
+        p0 = ro <= t0 ? p0 : 0.0f;
+        p1 = ro <= t1 ? p1 : 0.0f;
+      }
+      s0[r] = p0;
+      s1[r] = p1;
+      l += p0 + p1;
+    }
+    // O^T += V^T P^T over the tile's 64 keys
+#pragma unroll
+    for (int t = 0; t < PSTEPS; ++t) {
+      const Frag pf0 = acc_frag<T>(s0, t);
+      const Frag pf1 = acc_frag<T>(s1, t);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 0, t, 32 * mb, lane), pf0, oacc[mb]);
+        oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 32, t, 32 * mb, lane), pf1, oacc[mb]);
+      }
+    }
+  };
 
   load_tile(0);
   store_tile(0);
@@ -153,72 +227,18 @@ __global__ __launch_bounds__(kFwdThreads, 2) void fwd_kernel(FwdArgs a) {
     if (!CAUSAL || k0 <= qw + 31) {
       const T* kt = lds_k + buf * L::KTILE;
       const T* vt = lds_v + buf * L::VTILE;
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const T* krow = kt + (32 * kb + col) * L::KSTR;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          s[kb] = M::mma(row_frag<T>(krow + ks * M::KS, h), qf[ks], s[kb]);
-      }
-      // mask: keys past the end, and (causal) keys after the lane's query
       const bool edge = (k0 + kFwdBN > N) || (CAUSAL && k0 + kFwdBN - 1 > qw);
-      uint32_t live[2] = {0xffffffffu, 0xffffffffu};
-      if (edge) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + acc_row(r, h);
-            const bool ok = key < N && (!CAUSAL || key <= myq);
-            if (!ok) live[kb] &= ~(1u << r);
-          }
-        }
-      }
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = (live[kb] >> r) & 1u ? s[kb][r] : -__builtin_inff();
-          mx = __builtin_fmaxf(mx, x);
-        }
-      mx = halves_max(mx);
-      const float mt = mx > -__builtin_inff() ? mx * c : kMaxFloor;
-      const float mnew = __builtin_fmaxf(m, mt);
-      const float alpha = fast_exp2(m - mnew);
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -mnew));
-          p = (live[kb] >> r) & 1u ? p : 0.0f;
-          s[kb][r] = p;
-          rs += p;
-        }
-      rs = halves_sum(rs);
-      l = __builtin_fmaf(l, alpha, rs);
-      m = mnew;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
-      // O^T += V^T P^T over the tile's 64 keys
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < PSTEPS; ++t) {
-          const Frag pf = acc_frag<T>(s[kb], t);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 32 * kb, t, 32 * mb, lane), pf, oacc[mb]);
-        }
+      if (edge)
+        tile(kt, vt, k0, std::true_type{});
+      else
+        tile(kt, vt, k0, std::false_type{});
     }
     if (j + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // Epilogue: O = O_acc / l, LSE = ln(2^m * l).
+  l = halves_sum(l);
   if (myq < N) {
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     T* orow = reinterpret_cast<T*>(a.o) + head + (size_t)myq * D;
