@@ -186,6 +186,18 @@ __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane i's bytes land at
+// lds + 16 i (the LDS address must be wave-uniform).  The host pass of the
+// compiler does not know this builtin and would silently drop the kernel's host
+// stub, so only the device pass sees it.
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+#else
+  (void)r; (void)lds; (void)off;
+#endif
+}
+
 // Wave-uniform "does any lane want this".
 __device__ inline bool any_lane(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
 

@@ -64,6 +64,26 @@ struct FwdLayout {
 // weights 2^(c s - m) stay below 2^kTau, far inside fp32 and bf16 range.
 constexpr float kTau = 8.0f;
 
+#ifndef FA_FWD_SCHED
+#define FA_FWD_SCHED 0
+#endif
+#ifndef FA_FWD_PVORDER
+#define FA_FWD_PVORDER 0
+#endif
+
+// Ask the scheduler to interleave NM matrix ops with their LDS reads
+// (R reads per op), keeping the reads P ops ahead.
+template <int NM, int R, int P>
+__device__ inline void interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * P, 0);
+#pragma unroll
+  for (int i = 0; i < NM - P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) void fwd_kernel(FwdArgs a) {
   using M = Mma<T>;
@@ -164,6 +184,9 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
       s0 = M::mma(row_frag<T>(kr0 + ks * M::KS, h), qf[ks], s0);
       s1 = M::mma(row_frag<T>(kr1 + ks * M::KS, h), qf[ks], s1);
     }
+#if FA_FWD_SCHED
+    interleave<2 * KSTEPS, 1, 4>();
+#endif
     // key of register r in block kb is k0 + 32 kb + acc_row(r, h); allowed iff <= lim
     const int t0 = lim - k0 - 4 * h, t1 = t0 - 32;
     float mx = -__builtin_inff();
@@ -207,12 +230,24 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
     for (int t = 0; t < PSTEPS; ++t) {
       const Frag pf0 = acc_frag<T>(s0, t);
       const Frag pf1 = acc_frag<T>(s1, t);
+#if FA_FWD_PVORDER
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 0, t, 32 * mb, lane), pf0, oacc[mb]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 32, t, 32 * mb, lane), pf1, oacc[mb]);
+#else
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 0, t, 32 * mb, lane), pf0, oacc[mb]);
         oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 32, t, 32 * mb, lane), pf1, oacc[mb]);
       }
+#endif
     }
+#if FA_FWD_SCHED
+    interleave<2 * PSTEPS * MB, (sizeof(T) == 2 ? 2 : 1), 2>();
+#endif
   };
 
   load_tile(0);
@@ -275,12 +310,14 @@ static hipError_t launch_fwd_d(const FwdProblem& p, hipStream_t s) {
   return p.causal ? launch_fwd_t<T, 128, true>(p, s) : launch_fwd_t<T, 128, false>(p, s);
 }
 
+#ifndef FA_FWD16
+#define FA_FWD16 1
+#endif
+
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
-  switch (p.dtype) {
-    case 0: return launch_fwd_d<float>(p, s);
-    case 1: return launch_fwd_d<_Float16>(p, s);
-    default: return launch_fwd_d<__bf16>(p, s);
-  }
+  if (p.dtype == 0) return launch_fwd_d<float>(p, s);
+  if (FA_FWD16) return launch_fwd16(p, s);
+  return p.dtype == 1 ? launch_fwd_d<_Float16>(p, s) : launch_fwd_d<__bf16>(p, s);
 }
 
 }  // namespace fa

@@ -1,0 +1,310 @@
+// fa_fwd16.hip -- software-pipelined forward pass for 16-bit I/O (bf16, fp16) on gfx950.
+//
+// Same tiling as the generic forward (fa_fwd.hip): a workgroup of four waves
+// owns 128 query rows of one (batch, head); each wave keeps its 32 Q rows in
+// VGPRs and streams 64-key K/V tiles past them ("How Flash Attention Works:
+// Tiling, Softmax, GPU I/O", sections "Tiling Q, K, and V for Fast On-Chip
+// Memory" and "Online Softmax Without the Full Score Matrix").  What differs:
+//
+//  * K and V tiles go from device memory straight into LDS (buffer loads with
+//    the LDS destination), two stages each, so no VGPRs or LDS-write
+//    instructions are spent on staging.  Rows are packed back to back and the
+//    16-byte chunks of row r are permuted by XOR with sw(r), which keeps both
+//    the row-fragment reads of K and the transposing reads of V free of bank
+//    conflicts.
+//  * The work of tile j is software-pipelined against tile j-1 inside each
+//    wave: after S_j = K_j Q^T, the exponentials of tile j are issued together
+//    with the P_{j-1} V_{j-1} products, so the matrix cores run while the
+//    vector ALUs evaluate the softmax (the overlap FlashAttention-3 gets from
+//    warp specialisation on Hopper, "FlashAttention 1 vs 2 vs 3", done here
+//    within one wave).
+//  * Tiles that need no mask run a mask-free body whose LDS addresses are
+//    compile-time offsets from a handful of per-lane base registers.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+struct Fwd16Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int N;
+  int nqb;
+  int total;
+  float c;
+  int negate;
+};
+
+// 64-row tile of 16-bit rows in LDS, chunk-permuted (see the file comment).
+template <int D>
+struct Tile16 {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row: 8 or 16
+  static constexpr int BYTES = 64 * ROWB;        // 8 KiB or 16 KiB
+  static constexpr int ROUNDS = 64 * CPR / 256;  // direct loads per tile per wave (4 waves)
+  __device__ static constexpr int sw(int r) {
+    return CPR == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+  __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
+};
+
+// s_waitcnt vmcnt(0) with the other counters left alone.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
+  using M = Mma<T>;
+  using TL = Tile16<D>;
+  using Frag = typename M::Frag;
+  constexpr int KSTEPS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int KREG = 0;               // LDS regions: [K0 K1 V0 V1]
+  constexpr int VREG = 2 * TL::BYTES;
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TL::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int N = a.N;
+
+  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
+  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
+  if (CAUSAL) qb = a.nqb - 1 - qb;
+  const int q0 = qb * 128;
+  const int qw = q0 + wave * 32;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
+  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + head);
+  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + head);
+
+  const int myq = qw + col;
+  Frag qf[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
+    if (a.negate) qf[ks] = neg_frag<T>(qf[ks]);
+  }
+
+  const int nt_all = (N + 63) / 64;
+  int nt = nt_all;  // key tiles this block visits
+  if (CAUSAL) {
+    const int last = (q0 + 127) / 64 + 1;
+    nt = last < nt_all ? last : nt_all;
+  }
+  // tiles every wave of the block sees unmasked
+  const int nt_full = CAUSAL ? q0 / 64 : N / 64;
+  const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
+
+  // ---- direct loads: lane's source offset inside a tile, per round
+  uint32_t goff[TL::ROUNDS];
+#pragma unroll
+  for (int i = 0; i < TL::ROUNDS; ++i) {
+    const int s = (i * 4 + wave) * 64 + lane;
+    const int r = s / TL::CPR, pc = s % TL::CPR;
+    goff[i] = r * TL::ROWB + ((pc ^ TL::sw(r)) << 4);
+  }
+  auto dma = [&](const char* g, int row0, int region) {
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+#pragma unroll
+    for (int i = 0; i < TL::ROUNDS; ++i)
+      lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
+  };
+
+  // ---- LDS read addresses (per lane), relative to smem
+  uint32_t kaddr[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) kaddr[ks] = KREG + TL::phys(col, 2 * ks + h);
+  uint32_t vaddr[MB][2];
+  {
+    const int i = lane & 15, g = (lane >> 4) & 1;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 4 * h + (i >> 2) + 8 * hf;
+        const int chunk = 4 * mb + 2 * g + ((i & 3) >> 1);
+        vaddr[mb][hf] = VREG + TL::phys(row, chunk) + 8 * (i & 1);
+      }
+  }
+  auto kfrag = [&](int stage, int kb, int ks) {
+    const char* p = smem + kaddr[ks] + stage * TL::BYTES + kb * 32 * TL::ROWB;
+    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(p));
+  };
+  auto vfrag = [&](int stage, int kb, int t, int mb) {
+    const int off = stage * TL::BYTES + (32 * kb + 16 * t) * TL::ROWB;
+    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + vaddr[mb][0] + off));
+    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + vaddr[mb][1] + off));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(Frag, both);
+  };
+
+  f32x16 oacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
+  Frag pf[2][2];  // P of the previous tile, [32-key block][k-step], waiting for its V
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pf[kb][t] = zero_frag<T>();
+  float m = kMaxFloor;
+  float l = 0.0f;
+  const float c = a.c;
+
+  auto pv = [&](int vstage) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] = M::mma(vfrag(vstage, kb, t, mb), pf[kb][t], oacc[mb]);
+  };
+
+  // One pipeline step: S_j, softmax_j, and (if owed) O += P_{j-1} V_{j-1}.
+  // KST = j % 2 selects the stages: K_j in K stage KST, V_{j-1} in V stage KST^1.
+  auto step = [&](int j, auto kst_tag, auto full_tag) {
+    constexpr int KST = decltype(kst_tag)::value;
+    constexpr bool FULL = decltype(full_tag)::value;  // unmasked, and tile j-1 was done
+    wait_vmem();
+    __builtin_amdgcn_s_barrier();
+    if (j + 1 < nt) dma(Kg, 64 * (j + 1), KREG + (KST ^ 1) * TL::BYTES);
+    dma(Vg, 64 * j, VREG + KST * TL::BYTES);
+
+    const int k0 = 64 * j;
+    const bool act = FULL || !CAUSAL || k0 <= qw + 31;
+    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= qw + 31));
+    if (act) {
+      f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        s0 = M::mma(kfrag(KST, 0, ks), qf[ks], s0);
+        s1 = M::mma(kfrag(KST, 1, ks), qf[ks], s1);
+      }
+      const int t0 = lim - k0 - 4 * h, t1 = t0 - 32;
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ro = 8 * (r >> 2) + (r & 3);
+        float x0 = s0[r], x1 = s1[r];
+        if constexpr (!FULL) {
+          x0 = ro <= t0 ? x0 : -__builtin_inff();
+          x1 = ro <= t1 ? x1 : -__builtin_inff();
+        }
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(x0, x1));
+      }
+      mx = halves_max(mx);
+      float mt = mx * c;
+      if constexpr (!FULL) mt = mx > -__builtin_inff() ? mt : -__builtin_inff();
+      const bool need = any_lane(mt > m + 8.0f);
+      const float mnew = need ? __builtin_fmaxf(m, mt) : m;
+      const float alpha = fast_exp2(m - mnew);
+      const float negm = -mnew;
+      if (prev) pv(KST ^ 1);
+      float rs = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p0 = fast_exp2(__builtin_fmaf(s0[r], c, negm));
+        float p1 = fast_exp2(__builtin_fmaf(s1[r], c, negm));
+        if constexpr (!FULL) {
+          const int ro = 8 * (r >> 2) + (r & 3);
+          p0 = ro <= t0 ? p0 : 0.0f;
+          p1 = ro <= t1 ? p1 : 0.0f;
+        }
+        s0[r] = p0;
+        s1[r] = p1;
+        rs += p0 + p1;
+      }
+      if (need) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+        l *= alpha;
+      }
+      l += rs;
+      m = mnew;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        pf[0][t] = acc_frag<T>(s0, t);
+        pf[1][t] = acc_frag<T>(s1, t);
+      }
+    } else if (prev) {
+      pv(KST ^ 1);
+    }
+  };
+
+  dma(Kg, 0, KREG);
+  step(0, std::integral_constant<int, 0>{}, std::false_type{});
+  int j = 1;
+  for (; j + 1 < nt_full; j += 2) {
+    step(j, std::integral_constant<int, 1>{}, std::true_type{});
+    step(j + 1, std::integral_constant<int, 0>{}, std::true_type{});
+  }
+  if (j < nt_full) {
+    step(j, std::integral_constant<int, 1>{}, std::true_type{});
+    ++j;
+  }
+  for (; j < nt; ++j) {
+    if (j & 1)
+      step(j, std::integral_constant<int, 1>{}, std::false_type{});
+    else
+      step(j, std::integral_constant<int, 0>{}, std::false_type{});
+  }
+  // the last tile's P still owes its V product
+  wait_vmem();
+  __builtin_amdgcn_s_barrier();
+  if (!CAUSAL || 64 * (nt - 1) <= qw + 31) {
+    if ((nt - 1) & 1)
+      pv(1);
+    else
+      pv(0);
+  }
+
+  l = halves_sum(l);
+  if (myq < N) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    T* orow = reinterpret_cast<T*>(a.o) + head + (size_t)myq * D;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * mb + 8 * g + 4 * h;
+        store4<T>(orow + d0, oacc[mb][4 * g] * inv, oacc[mb][4 * g + 1] * inv, oacc[mb][4 * g + 2] * inv,
+                  oacc[mb][4 * g + 3] * inv);
+      }
+    if (a.lse != nullptr && h == 0)
+      a.lse[(size_t)bh * N + myq] = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
+  Fwd16Args a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
+  a.N = p.N;
+  a.nqb = (p.N + 127) / 128;
+  a.total = a.nqb * p.B * p.H;
+  const float sc = p.scale;
+  a.negate = sc < 0.0f;
+  a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
+  hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_fwd16_d(const FwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_fwd16_t<T, 64, true>(p, s) : launch_fwd16_t<T, 64, false>(p, s);
+  return p.causal ? launch_fwd16_t<T, 128, true>(p, s) : launch_fwd16_t<T, 128, false>(p, s);
+}
+
+hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s) {
+  return p.dtype == 1 ? launch_fwd16_d<_Float16>(p, s) : launch_fwd16_d<__bf16>(p, s);
+}
+
+}  // namespace fa
