@@ -53,6 +53,13 @@ struct Tile16 {
   __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
 };
 
+#ifndef FA16_PRIO
+#define FA16_PRIO 1
+#endif
+#ifndef FA16_SCHED
+#define FA16_SCHED 8
+#endif
+
 // s_waitcnt vmcnt(0) with the other counters left alone.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -183,13 +190,29 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= qw + 31));
     if (act) {
       f32x16 s0 = f32x16{}, s1 = f32x16{};
+#if FA16_PRIO
+      __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         s0 = M::mma(kfrag(KST, 0, ks), qf[ks], s0);
         s1 = M::mma(kfrag(KST, 1, ks), qf[ks], s1);
       }
+#if FA16_SCHED
+      // keep FA16_SCHED K-fragment reads in flight ahead of the matrix ops
+      __builtin_amdgcn_sched_group_barrier(0x100, FA16_SCHED, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KSTEPS - FA16_SCHED; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FA16_SCHED, 0);
+#endif
+#if FA16_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       const int t0 = lim - k0 - 4 * h, t1 = t0 - 32;
-      float mx = -__builtin_inff();
+      float xs[32];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ro = 8 * (r >> 2) + (r & 3);
@@ -198,8 +221,14 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
           x0 = ro <= t0 ? x0 : -__builtin_inff();
           x1 = ro <= t1 ? x1 : -__builtin_inff();
         }
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(x0, x1));
+        xs[2 * r] = x0;
+        xs[2 * r + 1] = x1;
       }
+      // 3-input max tree: 32 values in 16 v_max3
+      float mx = __builtin_fmaxf(xs[0], __builtin_fmaxf(xs[1], xs[2]));
+#pragma unroll
+      for (int r = 3; r + 1 < 32; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(xs[r], xs[r + 1]));
+      mx = __builtin_fmaxf(mx, xs[31]);
       mx = halves_max(mx);
       float mt = mx * c;
       if constexpr (!FULL) mt = mx > -__builtin_inff() ? mt : -__builtin_inff();
