@@ -435,7 +435,16 @@ static hipError_t launch_bwd_d(const BwdProblem& p, int stage, hipStream_t s) {
   return p.causal ? launch_bwd_t<T, 128, true>(p, stage, s) : launch_bwd_t<T, 128, false>(p, stage, s);
 }
 
+#ifndef FA_DQ16
+#define FA_DQ16 1
+#endif
+#ifndef FA_DKDV16
+#define FA_DKDV16 1
+#endif
+
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s) {
+  if (stage == 2 && p.dtype != 0 && FA_DQ16) return launch_dq16(p, s);
+  if (stage == 1 && p.dtype != 0 && FA_DKDV16) return launch_dkdv16(p, s);
   switch (p.dtype) {
     case 0: return launch_bwd_d<float>(p, stage, s);
     case 1: return launch_bwd_d<_Float16>(p, stage, s);

@@ -1,0 +1,487 @@
+// fa_bwd16.hip -- backward kernels for 16-bit I/O (bf16, fp16) on gfx950.
+//
+// Same algorithm and outputs as the generic backward (fa_bwd.hip): the score
+// tiles are recomputed from Q, K and the forward's log-sum-exp, never stored
+// ("How Flash Attention Works: Tiling, Softmax, GPU I/O", section "The
+// Backward Pass: Recomputation Instead of Stored Activations"), and
+//   P = exp(scale S - LSE), dP = dO V^T, dS = P (dP - D),
+//   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+// The 16-bit kernels use the machinery of the pipelined forward
+// (fa_fwd16.hip): streamed tiles go straight from device memory into LDS with
+// buffer loads, rows packed and chunk-permuted by Tile16::sw so row reads and
+// transposing reads avoid bank conflicts, and the products of one tile are
+// software-pipelined against the element-wise work of the next.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_tile16.h"
+
+namespace fa {
+
+struct Bwd16Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* dvec;
+  void* dq;
+  void* dk;
+  void* dv;
+  int N;
+  int nblk;
+  int total;
+  float c;      // scale * log2(e), signed
+  float scale;
+};
+
+#ifndef FA_DQ_PRIO
+#define FA_DQ_PRIO 1
+#endif
+
+// --------------------------------------------------------------------------
+// dQ: a workgroup owns 128 queries (32 per wave, Q and dO rows in VGPRs) and
+// streams 64-key K/V tiles.  Step j computes S^T_j = K_j Q^T and
+// dP^T_j = V_j dO^T, then forms dS^T_j while the matrix cores accumulate
+// dQ^T += K_{j-1}^T dS^T_{j-1}.  LDS: K in three stages (K_{j-1}, K_j and the
+// one being loaded), V in two.
+#ifndef FA_DQ_OCC128
+#define FA_DQ_OCC128 2
+#endif
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(Bwd16Args a) {
+  using M = Mma<T>;
+  using TL = Tile16<D>;
+  using Frag = typename M::Frag;
+  constexpr int KSTEPS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int KREG = 0;                // [K0 K1 K2 V0 V1]
+  constexpr int VREG = 3 * TL::BYTES;
+
+  __shared__ __attribute__((aligned(1024))) char smem[5 * TL::BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int N = a.N;
+
+  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
+  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
+  if (CAUSAL) qb = a.nblk - 1 - qb;
+  const int q0 = qb * 128;
+  const int qw = q0 + wave * 32;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
+  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + head;
+  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + head);
+  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + head);
+
+  const int myq = qw + col;
+  Frag qf[KSTEPS], dof[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
+    dof[ks] = myq < N ? row_frag<T>(dO + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
+  }
+  const float lse2 = myq < N ? a.lse[(size_t)bh * N + myq] * kLog2e : 0.0f;
+  const float dd = myq < N ? a.dvec[(size_t)bh * N + myq] : 0.0f;
+
+  const int nt_all = (N + 63) / 64;
+  int nt = nt_all;
+  if (CAUSAL) {
+    const int last = (q0 + 127) / 64 + 1;
+    nt = last < nt_all ? last : nt_all;
+  }
+  const int nt_full = CAUSAL ? q0 / 64 : N / 64;
+  const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
+
+  uint32_t goff[TL::ROUNDS];
+  tile16_load_offsets<D>(goff, wave, lane);
+  auto dma = [&](const char* g, int row0, int region) {
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+#pragma unroll
+    for (int i = 0; i < TL::ROUNDS; ++i) lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
+  };
+
+  uint32_t krow[KSTEPS], vrow[KSTEPS], ktr[MB][2];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    krow[ks] = KREG + tile16_row_addr<D>(col, ks, h);
+    vrow[ks] = VREG + tile16_row_addr<D>(col, ks, h);
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) ktr[mb][hf] = KREG + tile16_tr_addr<D>(lane, mb, hf);
+
+  f32x16 dqacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) dqacc[mb] = f32x16{};
+  Frag dsf[2][2];  // dS^T of the previous tile, [32-key block][k-step]
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) dsf[kb][t] = zero_frag<T>();
+  const float c = a.c;
+
+  auto dq_prev = [&](auto kps) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          dqacc[mb] = M::mma(tile16_tr_frag<T, D>(smem, ktr[mb][0], ktr[mb][1], kps * TL::BYTES + (32 * kb + 16 * t) * TL::ROWB),
+                             dsf[kb][t], dqacc[mb]);
+  };
+
+  // Step j: K_j in K stage ks3 = j % 3, V_j in V stage vs2 = j % 2, K_{j-1} in (j - 1) % 3.
+  auto step = [&](int j, auto ks3, auto vs2, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int kps = ks3 == 0 ? 2 : ks3 - 1;
+    wait_vmem();
+    __builtin_amdgcn_s_barrier();
+    if (j + 1 < nt) {
+      const int kn = ks3 == 2 ? 0 : ks3 + 1;
+      dma(Kg, 64 * (j + 1), KREG + kn * TL::BYTES);
+      dma(Vg, 64 * (j + 1), VREG + (vs2 ^ 1) * TL::BYTES);
+    }
+    const int k0 = 64 * j;
+    const bool act = FULL || !CAUSAL || k0 <= qw + 31;
+    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= qw + 31));
+    if (act) {
+      const int t0 = lim - k0 - 4 * h;
+      // the two 32-key halves one after the other keeps two accumulators live, not four
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#if FA_DQ_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
+        f32x16 s = f32x16{}, p = f32x16{};
+        const int ko = ks3 * TL::BYTES + kb * 32 * TL::ROWB, vo = vs2 * TL::BYTES + kb * 32 * TL::ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          s = M::mma(tile16_row_frag<T>(smem, krow[ks] + ko), qf[ks], s);
+          p = M::mma(tile16_row_frag<T>(smem, vrow[ks] + vo), dof[ks], p);
+        }
+#if FA_DQ_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
+        if (kb == 0 && prev) dq_prev(kps);
+        const int tk = t0 - 32 * kb;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+          if constexpr (!FULL) {
+            const int ro = 8 * (r >> 2) + (r & 3);
+            e = ro <= tk ? e : 0.0f;
+          }
+          p[r] = e * (p[r] - dd);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) dsf[kb][t] = acc_frag<T>(p, t);
+      }
+    } else if (prev) {
+      dq_prev(kps);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  dma(Kg, 0, KREG);
+  dma(Vg, 0, VREG);
+  // tile 0 owes no dQ product yet: generic step
+  step(0, 0, 0, std::false_type{});
+  int j = 1;
+  // mask-free steps, six at a time so that every LDS offset is a constant
+  for (; j + 5 < nt_full; j += 6) {
+    step(j, I1{}, I1{}, std::true_type{});
+    step(j + 1, I2{}, I0{}, std::true_type{});
+    step(j + 2, I0{}, I1{}, std::true_type{});
+    step(j + 3, I1{}, I0{}, std::true_type{});
+    step(j + 4, I2{}, I1{}, std::true_type{});
+    step(j + 5, I0{}, I0{}, std::true_type{});
+  }
+  // the rest (up to five mask-free tiles, then the masked ones): runtime stages
+  for (; j < nt; ++j) {
+    if (j < nt_full)
+      step(j, j % 3, j & 1, std::true_type{});
+    else
+      step(j, j % 3, j & 1, std::false_type{});
+  }
+  wait_vmem();
+  __builtin_amdgcn_s_barrier();
+  if (!CAUSAL || 64 * (nt - 1) <= qw + 31) dq_prev((nt - 1) % 3);
+
+  if (myq < N) {
+    T* row = reinterpret_cast<T*>(a.dq) + head + (size_t)myq * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * mb + 8 * g + 4 * h;
+        store4<T>(row + d0, dqacc[mb][4 * g] * sc, dqacc[mb][4 * g + 1] * sc, dqacc[mb][4 * g + 2] * sc,
+                  dqacc[mb][4 * g + 3] * sc);
+      }
+  }
+}
+
+// --------------------------------------------------------------------------
+// dK, dV: a workgroup owns 128 keys (32 per wave; K and V rows in VGPRs as
+// the stationary B operands) and streams 64-query tiles of Q and dO, with the
+// query rows' LSE (pre-scaled to log2 units) and D, through LDS.  Per
+// 32-query half: S = Q K^T and dP = dO V^T, then P and dS element-wise, then
+// dV^T += dO^T P and dK^T += Q^T dS with the transposing reads of dO and Q.
+// The four accumulators (dK^T, dV^T) and the stationary fragments need about
+// 280 VGPRs, so one wave per SIMD runs this kernel; the element-wise work of
+// one half overlaps the matrix ops of the other inside the wave.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
+  using M = Mma<T>;
+  using TL = Tile16<D>;
+  using Frag = typename M::Frag;
+  constexpr int KSTEPS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int QREG = 0;                  // [Q0 Q1 dO0 dO1 lse0 lse1 D0 D1]
+  constexpr int OREG = 2 * TL::BYTES;
+  constexpr int LREG = 4 * TL::BYTES;      // 2 x 64 floats of -LSE * log2(e)
+  constexpr int DREG = LREG + 512;         // 2 x 64 floats of D
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TL::BYTES + 1024];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int N = a.N;
+
+  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
+  const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
+  const int kb0 = kblk * 128;
+  const int kw = kb0 + 32 * wave;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const char* Qg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + head);
+  const char* Og = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + head);
+  const float* lse = a.lse + (size_t)bh * N;
+  const float* dvec = a.dvec + (size_t)bh * N;
+
+  const int mykey = kw + col;
+  Frag kf[KSTEPS], vf[KSTEPS];
+  {
+    const T* Kp = reinterpret_cast<const T*>(a.k) + head;
+    const T* Vp = reinterpret_cast<const T*>(a.v) + head;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      kf[ks] = mykey < N ? row_frag<T>(Kp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
+      vf[ks] = mykey < N ? row_frag<T>(Vp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
+    }
+  }
+
+  const int nt = (N + 63) / 64;
+  const int first = CAUSAL ? kb0 / 64 : 0;
+  // query tiles every wave sees unmasked: [full0, full1)
+  const int full0 = CAUSAL ? (kb0 + 127) / 64 + 1 : 0;
+  const int full1 = N / 64;
+
+  uint32_t goff[TL::ROUNDS];
+  tile16_load_offsets<D>(goff, wave, lane);
+  float lse_next = 0.0f, d_next = 0.0f;  // wave 0 stages the next tile's per-row values
+  auto fetch = [&](int i, int stage) {
+    const int row0 = 64 * i;
+    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+#pragma unroll
+    for (int r = 0; r < TL::ROUNDS; ++r) {
+      lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * 4 + wave) * 1024, goff[r]);
+      lds_load16(ro, smem + OREG + stage * TL::BYTES + (r * 4 + wave) * 1024, goff[r]);
+    }
+    if (wave == 0) {
+      const int qi = row0 + lane;
+      lse_next = qi < N ? -lse[qi] * kLog2e : 0.0f;
+      d_next = qi < N ? dvec[qi] : 0.0f;
+    }
+  };
+  auto publish = [&](int stage) {  // wave 0 writes the staged per-row values
+    if (wave == 0) {
+      reinterpret_cast<float*>(smem + LREG)[stage * 64 + lane] = lse_next;
+      reinterpret_cast<float*>(smem + DREG)[stage * 64 + lane] = d_next;
+    }
+  };
+
+  uint32_t qrow[KSTEPS], qtr[MB][2];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) qrow[ks] = tile16_row_addr<D>(col, ks, h);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) qtr[mb][hf] = tile16_tr_addr<D>(lane, mb, hf);
+
+  f32x16 dkacc[MB], dvacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    dkacc[mb] = f32x16{};
+    dvacc[mb] = f32x16{};
+  }
+  const float c = a.c;
+
+  // Step i: query tile i in stage st; the next tile is fetched into st ^ 1.
+  auto step = [&](int i, auto st, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    wait_vmem();
+    publish(st);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS writes done (lgkmcnt(0))
+    __builtin_amdgcn_s_barrier();
+    if (i + 1 < nt) fetch(i + 1, st ^ 1);
+    const int i0 = 64 * i;
+    if (!FULL && CAUSAL && i0 + 63 < kw) return;  // every query of the tile precedes this wave's keys
+    const int qo = QREG + st * TL::BYTES, oo = OREG + st * TL::BYTES;
+    const float* lt = reinterpret_cast<const float*>(smem + LREG) + st * 64;
+    const float* dt = reinterpret_cast<const float*>(smem + DREG) + st * 64;
+    Frag pf[2][2], sf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        s = M::mma(tile16_row_frag<T>(smem, qrow[ks] + qo + 32 * qb * TL::ROWB), kf[ks], s);
+        dp = M::mma(tile16_row_frag<T>(smem, qrow[ks] + oo + 32 * qb * TL::ROWB), vf[ks], dp);
+      }
+      // rows of s / dp: queries i0 + 32 qb + acc_row(r, h); column: key mykey
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int rr = 32 * qb + 8 * g + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rr);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g + u;
+          float p = fast_exp2(__builtin_fmaf(s[r], c, l4[u]));
+          if constexpr (!FULL) {
+            const int qi = i0 + rr + u;
+            p = (qi < N && (!CAUSAL || mykey <= qi)) ? p : 0.0f;
+          }
+          s[r] = p;
+          dp[r] = p * (dp[r] - d4[u]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        pf[qb][t] = acc_frag<T>(s, t);
+        sf[qb][t] = acc_frag<T>(dp, t);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int off = (32 * qb + 16 * t) * TL::ROWB;
+          dvacc[mb] = M::mma(tile16_tr_frag<T, D>(smem, qtr[mb][0] + oo, qtr[mb][1] + oo, off), pf[qb][t], dvacc[mb]);
+          dkacc[mb] = M::mma(tile16_tr_frag<T, D>(smem, qtr[mb][0] + qo, qtr[mb][1] + qo, off), sf[qb][t], dkacc[mb]);
+        }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (first < nt) {
+    fetch(first, 0);
+    int i = first;
+    for (; i < nt && i < full0; ++i) {
+      if ((i - first) & 1)
+        step(i, I1{}, std::false_type{});
+      else
+        step(i, I0{}, std::false_type{});
+    }
+    // mask-free tiles, two at a time (constant LDS offsets)
+    for (; i + 1 < full1; i += 2) {
+      if ((i - first) & 1) {
+        step(i, I1{}, std::true_type{});
+        step(i + 1, I0{}, std::true_type{});
+      } else {
+        step(i, I0{}, std::true_type{});
+        step(i + 1, I1{}, std::true_type{});
+      }
+    }
+    for (; i < nt; ++i) {
+      const bool full = i < full1;
+      if ((i - first) & 1) {
+        if (full) step(i, I1{}, std::true_type{}); else step(i, I1{}, std::false_type{});
+      } else {
+        if (full) step(i, I0{}, std::true_type{}); else step(i, I0{}, std::false_type{});
+      }
+    }
+  }
+
+  if (mykey < N) {
+    T* dkrow = reinterpret_cast<T*>(a.dk) + head + (size_t)mykey * D;
+    T* dvrow = reinterpret_cast<T*>(a.dv) + head + (size_t)mykey * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * mb + 8 * g + 4 * h;
+        store4<T>(dkrow + d0, dkacc[mb][4 * g] * sc, dkacc[mb][4 * g + 1] * sc, dkacc[mb][4 * g + 2] * sc,
+                  dkacc[mb][4 * g + 3] * sc);
+        store4<T>(dvrow + d0, dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2], dvacc[mb][4 * g + 3]);
+      }
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
+  Bwd16Args a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
+  a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
+  a.N = p.N;
+  a.scale = p.scale;
+  a.c = p.scale * kLog2e;
+  a.nblk = (p.N + 127) / 128;
+  a.total = a.nblk * p.B * p.H;
+  hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dkdv16_d(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_dkdv16_t<T, 64, true>(p, s) : launch_dkdv16_t<T, 64, false>(p, s);
+  return p.causal ? launch_dkdv16_t<T, 128, true>(p, s) : launch_dkdv16_t<T, 128, false>(p, s);
+}
+
+hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s) {
+  return p.dtype == 1 ? launch_dkdv16_d<_Float16>(p, s) : launch_dkdv16_d<__bf16>(p, s);
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_dq16_t(const BwdProblem& p, hipStream_t stream) {
+  Bwd16Args a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
+  a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
+  a.N = p.N;
+  a.scale = p.scale;
+  a.c = p.scale * kLog2e;
+  a.nblk = (p.N + 127) / 128;
+  a.total = a.nblk * p.B * p.H;
+  hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dq16_d(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_dq16_t<T, 64, true>(p, s) : launch_dq16_t<T, 64, false>(p, s);
+  return p.causal ? launch_dq16_t<T, 128, true>(p, s) : launch_dq16_t<T, 128, false>(p, s);
+}
+
+hipError_t launch_dq16(const BwdProblem& p, hipStream_t s) {
+  return p.dtype == 1 ? launch_dq16_d<_Float16>(p, s) : launch_dq16_d<__bf16>(p, s);
+}
+
+}  // namespace fa

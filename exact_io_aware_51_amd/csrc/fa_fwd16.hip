@@ -24,6 +24,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_tile16.h"
 
 namespace fa {
 
@@ -40,28 +41,12 @@ struct Fwd16Args {
   int negate;
 };
 
-// 64-row tile of 16-bit rows in LDS, chunk-permuted (see the file comment).
-template <int D>
-struct Tile16 {
-  static constexpr int ROWB = 2 * D;
-  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row: 8 or 16
-  static constexpr int BYTES = 64 * ROWB;        // 8 KiB or 16 KiB
-  static constexpr int ROUNDS = 64 * CPR / 256;  // direct loads per tile per wave (4 waves)
-  __device__ static constexpr int sw(int r) {
-    return CPR == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-  }
-  __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
-};
-
 #ifndef FA16_PRIO
 #define FA16_PRIO 1
 #endif
 #ifndef FA16_SCHED
 #define FA16_SCHED 8
 #endif
-
-// s_waitcnt vmcnt(0) with the other counters left alone.
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
@@ -112,12 +97,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 
   // ---- direct loads: lane's source offset inside a tile, per round
   uint32_t goff[TL::ROUNDS];
-#pragma unroll
-  for (int i = 0; i < TL::ROUNDS; ++i) {
-    const int s = (i * 4 + wave) * 64 + lane;
-    const int r = s / TL::CPR, pc = s % TL::CPR;
-    goff[i] = r * TL::ROWB + ((pc ^ TL::sw(r)) << 4);
-  }
+  tile16_load_offsets<D>(goff, wave, lane);
   auto dma = [&](const char* g, int row0, int region) {
     const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
 #pragma unroll
@@ -128,30 +108,17 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   // ---- LDS read addresses (per lane), relative to smem
   uint32_t kaddr[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) kaddr[ks] = KREG + TL::phys(col, 2 * ks + h);
+  for (int ks = 0; ks < KSTEPS; ++ks) kaddr[ks] = KREG + tile16_row_addr<D>(col, ks, h);
   uint32_t vaddr[MB][2];
-  {
-    const int i = lane & 15, g = (lane >> 4) & 1;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int row = 4 * h + (i >> 2) + 8 * hf;
-        const int chunk = 4 * mb + 2 * g + ((i & 3) >> 1);
-        vaddr[mb][hf] = VREG + TL::phys(row, chunk) + 8 * (i & 1);
-      }
-  }
+    for (int hf = 0; hf < 2; ++hf) vaddr[mb][hf] = VREG + tile16_tr_addr<D>(lane, mb, hf);
   auto kfrag = [&](int stage, int kb, int ks) {
-    const char* p = smem + kaddr[ks] + stage * TL::BYTES + kb * 32 * TL::ROWB;
-    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(p));
+    return tile16_row_frag<T>(smem, kaddr[ks] + stage * TL::BYTES + kb * 32 * TL::ROWB);
   };
   auto vfrag = [&](int stage, int kb, int t, int mb) {
-    const int off = stage * TL::BYTES + (32 * kb + 16 * t) * TL::ROWB;
-    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + vaddr[mb][0] + off));
-    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + vaddr[mb][1] + off));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
-    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(Frag, both);
+    return tile16_tr_frag<T, D>(smem, vaddr[mb][0], vaddr[mb][1], stage * TL::BYTES + (32 * kb + 16 * t) * TL::ROWB);
   };
 
   f32x16 oacc[MB];

@@ -39,5 +39,7 @@ hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s);  // bf16 / fp16 only
 // stage: 0 = row sums D, 1 = dK/dV, 2 = dQ
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
+hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only
+hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s);  // bf16 / fp16 only
 
 }  // namespace fa
