@@ -444,7 +444,6 @@ static hipError_t launch_bwd_d(const BwdProblem& p, int stage, hipStream_t s) {
 
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s) {
   if (stage == 2 && p.dtype != 0 && FA_DQ16) return launch_dq16(p, s);
-  if (stage == 1 && p.dtype != 0 && FA_DKDV16 == 2) return launch_dkdv8(p, s);
   if (stage == 1 && p.dtype != 0 && FA_DKDV16) return launch_dkdv16(p, s);
   switch (p.dtype) {
     case 0: return launch_bwd_d<float>(p, stage, s);

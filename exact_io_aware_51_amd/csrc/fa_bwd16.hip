@@ -492,234 +492,6 @@ hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s) {
   return p.dtype == 1 ? launch_dkdv16_d<_Float16>(p, s) : launch_dkdv16_d<__bf16>(p, s);
 }
 
-// --------------------------------------------------------------------------
-// dK and dV with eight waves per workgroup: 128 keys, 32 per wave pair.
-// Waves 0-3 accumulate dV^T += dO^T P (stationary: K rows); waves 4-7
-// accumulate dK^T += Q^T dS with dS = P (dP - D), dP = dO V^T (stationary: K
-// and V rows).  Both halves stream the same 64-query tiles of Q and dO (and
-// the rows' LSE, pre-scaled to log2 units, and D) through LDS.  Each dV wave
-// recomputes the S its partner also computes, but neither wave needs more than
-// one long-lived accumulator, so a dV wave and a dK wave share every SIMD and
-// the lighter dV work fills the heavier dK wave's gaps.
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void dkdv8_kernel(Bwd16Args a) {
-  using M = Mma<T>;
-  using TL = Tile16<D>;
-  using Frag = typename M::Frag;
-  constexpr int KSTEPS = D / 16;
-  constexpr int MB = D / 32;
-  constexpr int ROUNDS = 64 * TL::CPR / 512;  // direct loads per tile per wave (8 waves)
-  constexpr int QREG = 0;                      // [Q0 Q1 dO0 dO1 lse0 lse1 D0 D1]
-  constexpr int OREG = 2 * TL::BYTES;
-  constexpr int LREG = 4 * TL::BYTES;
-  constexpr int DREG = LREG + 512;
-
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TL::BYTES + 1024];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool dkw = wave >= 4;  // wave-uniform: this wave accumulates dK (else dV)
-  const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
-
-  const int bid = xcd_remap(blockIdx.x, a.total);
-  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
-  const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
-  const int kb0 = kblk * 128;
-  const int kw = kb0 + 32 * (wave & 3);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const char* Qg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + head);
-  const char* Og = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + head);
-  const float* lse = a.lse + (size_t)bh * N;
-  const float* dvec = a.dvec + (size_t)bh * N;
-
-  const int mykey = kw + col;
-  const int nt = (N + 63) / 64;
-  const int first = CAUSAL ? kb0 / 64 : 0;
-  const int full0 = CAUSAL ? (kb0 + 127) / 64 + 1 : 0;  // first query tile every wave sees unmasked
-  const int full1 = N / 64;
-
-  uint32_t goff[ROUNDS];
-#pragma unroll
-  for (int i = 0; i < ROUNDS; ++i) {
-    const int sl = (i * 8 + wave) * 64 + lane;
-    const int r = sl / TL::CPR, pc = sl % TL::CPR;
-    goff[i] = r * TL::ROWB + ((pc ^ TL::sw(r)) << 4);
-  }
-  float lse_next = 0.0f, d_next = 0.0f;  // wave 0 stages the next tile's per-row values
-  auto fetch = [&](int i, int stage) {
-    const int row0 = 64 * i;
-    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
-    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
-#pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * 8 + wave) * 1024, goff[r]);
-      lds_load16(ro, smem + OREG + stage * TL::BYTES + (r * 8 + wave) * 1024, goff[r]);
-    }
-    if (wave == 0) {
-      const int qi = row0 + lane;
-      lse_next = qi < N ? -lse[qi] * kLog2e : 0.0f;
-      d_next = qi < N ? dvec[qi] : 0.0f;
-    }
-  };
-  auto publish = [&](int stage) {
-    if (wave == 0) {
-      reinterpret_cast<float*>(smem + LREG)[stage * 64 + lane] = lse_next;
-      reinterpret_cast<float*>(smem + DREG)[stage * 64 + lane] = d_next;
-    }
-  };
-
-  uint32_t qrow[KSTEPS], qtr[MB][2];
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) qrow[ks] = tile16_row_addr<D>(col, ks, h);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) qtr[mb][hf] = tile16_tr_addr<D>(lane, mb, hf);
-
-  const float c = a.c;
-
-  // The per-wave pass over all query tiles; DK selects the gradient.
-  auto run = [&](auto dk_tag) {
-    constexpr bool DK = decltype(dk_tag)::value;
-    Frag kf[KSTEPS], vf[DK ? KSTEPS : 1];
-    {
-      const T* Kp = reinterpret_cast<const T*>(a.k) + head;
-      const T* Vp = reinterpret_cast<const T*>(a.v) + head;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        kf[ks] = mykey < N ? row_frag<T>(Kp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
-        if constexpr (DK) vf[ks] = mykey < N ? row_frag<T>(Vp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
-      }
-    }
-    f32x16 acc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
-
-    auto step = [&](int i, auto st, auto full_tag) {
-      constexpr bool FULL = decltype(full_tag)::value;
-      wait_vmem();
-      publish(st);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS writes done (lgkmcnt(0))
-      __builtin_amdgcn_s_barrier();
-      if (i + 1 < nt) fetch(i + 1, st ^ 1);
-      const int i0 = 64 * i;
-      if (!FULL && CAUSAL && i0 + 63 < kw) return;  // every query of the tile precedes these keys
-      const int qo = QREG + st * TL::BYTES, oo = OREG + st * TL::BYTES;
-      const int to = DK ? qo : oo;  // the operand whose transpose multiplies dS (dK) or P (dV)
-      const float* lt = reinterpret_cast<const float*>(smem + LREG) + st * 64;
-      const float* dt = reinterpret_cast<const float*>(smem + DREG) + st * 64;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          s = M::mma(tile16_row_frag<T>(smem, qrow[ks] + qo + 32 * qb * TL::ROWB), kf[ks], s);
-          if constexpr (DK) dp = M::mma(tile16_row_frag<T>(smem, qrow[ks] + oo + 32 * qb * TL::ROWB), vf[ks], dp);
-        }
-        // rows of s / dp: queries i0 + 32 qb + acc_row(r, h); column: key mykey
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rr = 32 * qb + 8 * g + 4 * h;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
-          f32x4 d4 = f32x4{};
-          if constexpr (DK) d4 = *reinterpret_cast<const f32x4*>(dt + rr);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * g + u;
-            float p = fast_exp2(__builtin_fmaf(s[r], c, l4[u]));
-            if constexpr (!FULL) {
-              const int qi = i0 + rr + u;
-              p = (qi < N && (!CAUSAL || mykey <= qi)) ? p : 0.0f;
-            }
-            s[r] = DK ? p * (dp[r] - d4[u]) : p;
-          }
-        }
-        Frag f[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) f[t] = acc_frag<T>(s, t);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb] = M::mma(tile16_tr_frag<T, D>(smem, qtr[mb][0] + to, qtr[mb][1] + to, (32 * qb + 16 * t) * TL::ROWB),
-                             f[t], acc[mb]);
-      }
-    };
-
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    if (first < nt) {
-      fetch(first, 0);
-      int i = first;
-      for (; i < nt && i < full0; ++i) {
-        if ((i - first) & 1)
-          step(i, I1{}, std::false_type{});
-        else
-          step(i, I0{}, std::false_type{});
-      }
-      for (; i + 1 < full1; i += 2) {  // mask-free tiles, two at a time (constant LDS offsets)
-        if ((i - first) & 1) {
-          step(i, I1{}, std::true_type{});
-          step(i + 1, I0{}, std::true_type{});
-        } else {
-          step(i, I0{}, std::true_type{});
-          step(i + 1, I1{}, std::true_type{});
-        }
-      }
-      for (; i < nt; ++i) {
-        const bool full = i < full1;
-        if ((i - first) & 1) {
-          if (full) step(i, I1{}, std::true_type{}); else step(i, I1{}, std::false_type{});
-        } else {
-          if (full) step(i, I0{}, std::true_type{}); else step(i, I0{}, std::false_type{});
-        }
-      }
-    }
-    if (mykey < N) {
-      T* row = reinterpret_cast<T*>(DK ? a.dk : a.dv) + head + (size_t)mykey * D;
-      const float sc = DK ? a.scale : 1.0f;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * mb + 8 * g + 4 * h;
-          store4<T>(row + d0, acc[mb][4 * g] * sc, acc[mb][4 * g + 1] * sc, acc[mb][4 * g + 2] * sc,
-                    acc[mb][4 * g + 3] * sc);
-        }
-    }
-  };
-  if (dkw)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
-}
-
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_dkdv8_t(const BwdProblem& p, hipStream_t stream) {
-  Bwd16Args a;
-  a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
-  a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
-  a.N = p.N;
-  a.scale = p.scale;
-  a.c = p.scale * kLog2e;
-  a.nblk = (p.N + 127) / 128;
-  a.total = a.nblk * p.B * p.H;
-  hipLaunchKernelGGL((dkdv8_kernel<T, D, CAUSAL>), dim3(a.total), dim3(512), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <typename T>
-static hipError_t launch_dkdv8_d(const BwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_dkdv8_t<T, 64, true>(p, s) : launch_dkdv8_t<T, 64, false>(p, s);
-  return p.causal ? launch_dkdv8_t<T, 128, true>(p, s) : launch_dkdv8_t<T, 128, false>(p, s);
-}
-
-hipError_t launch_dkdv8(const BwdProblem& p, hipStream_t s) {
-  return p.dtype == 1 ? launch_dkdv8_d<_Float16>(p, s) : launch_dkdv8_d<__bf16>(p, s);
-}
-
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_dq16_t(const BwdProblem& p, hipStream_t stream) {
   Bwd16Args a;

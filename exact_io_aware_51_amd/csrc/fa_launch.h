@@ -41,6 +41,5 @@ hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s);  // bf16 / fp16 onl
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only
 hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s);  // bf16 / fp16 only
-hipError_t launch_dkdv8(const BwdProblem& p, hipStream_t s);   // bf16 / fp16 only, 8 waves
 
 }  // namespace fa
