@@ -67,7 +67,7 @@ __device__ inline void reads_ahead() {
 // dQ^T += K_{j-1}^T dS^T_{j-1}.  LDS: K in three stages (K_{j-1}, K_j and the
 // one being loaded), V in two.
 #ifndef FA_DQ_OCC128
-#define FA_DQ_OCC128 2
+#define FA_DQ_OCC128 1
 #endif
 
 template <typename T, int D, bool CAUSAL>

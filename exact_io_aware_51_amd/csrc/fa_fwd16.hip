@@ -20,6 +20,13 @@
 //    within one wave).
 //  * Tiles that need no mask run a mask-free body whose LDS addresses are
 //    compile-time offsets from a handful of per-lane base registers.
+//  * In that body the exponentials are taken against the running maximum
+//    before this tile's maximum is known; the row sums they produce bound
+//    every p, so the maximum (a 30-instruction tree per lane) is only formed
+//    when a sum shows that some p may exceed 2^8, and the tile is then redone
+//    against the new maximum.  Either way each p is exp2 of its score minus a
+//    maximum that is at most 8 below the true running one, as in the lazy
+//    rescale of the generic kernel, and the result is the same softmax.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -44,14 +51,23 @@ struct Fwd16Args {
 #ifndef FA16_PRIO
 #define FA16_PRIO 1
 #endif
+#ifndef FA16_SPEC
+#define FA16_SPEC 1
+#endif
 #ifndef FA16_SCHED
 #define FA16_SCHED 8
 #endif
 
+#ifndef FA_FWD_BN64
+#define FA_FWD_BN64 64
+#endif
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
+  constexpr int BN = D == 64 ? FA_FWD_BN64 : 64;  // keys per tile
+  constexpr int KB = BN / 32;                      // 32-key blocks per tile
   using M = Mma<T>;
-  using TL = Tile16<D>;
+  using TL = Tile16<D, BN>;
   using Frag = typename M::Frag;
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
@@ -85,19 +101,19 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     if (a.negate) qf[ks] = neg_frag<T>(qf[ks]);
   }
 
-  const int nt_all = (N + 63) / 64;
+  const int nt_all = (N + BN - 1) / BN;
   int nt = nt_all;  // key tiles this block visits
   if (CAUSAL) {
-    const int last = (q0 + 127) / 64 + 1;
+    const int last = (q0 + 127) / BN + 1;
     nt = last < nt_all ? last : nt_all;
   }
   // tiles every wave of the block sees unmasked
-  const int nt_full = CAUSAL ? q0 / 64 : N / 64;
+  const int nt_full = CAUSAL ? q0 / BN : N / BN;
   const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
 
   // ---- direct loads: lane's source offset inside a tile, per round
   uint32_t goff[TL::ROUNDS];
-  tile16_load_offsets<D>(goff, wave, lane);
+  tile16_load_offsets<D, BN>(goff, wave, lane);
   auto dma = [&](const char* g, int row0, int region) {
     const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
 #pragma unroll
@@ -124,9 +140,9 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   f32x16 oacc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x16{};
-  Frag pf[2][2];  // P of the previous tile, [32-key block][k-step], waiting for its V
+  Frag pf[KB][2];  // P of the previous tile, [32-key block][k-step], waiting for its V
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) pf[kb][t] = zero_frag<T>();
   float m = kMaxFloor;
@@ -135,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 
   auto pv = [&](int vstage) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -149,27 +165,28 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     constexpr bool FULL = decltype(full_tag)::value;  // unmasked, and tile j-1 was done
     wait_vmem();
     __builtin_amdgcn_s_barrier();
-    if (j + 1 < nt) dma(Kg, 64 * (j + 1), KREG + (KST ^ 1) * TL::BYTES);
-    dma(Vg, 64 * j, VREG + KST * TL::BYTES);
+    if (j + 1 < nt) dma(Kg, BN * (j + 1), KREG + (KST ^ 1) * TL::BYTES);
+    dma(Vg, BN * j, VREG + KST * TL::BYTES);
 
-    const int k0 = 64 * j;
+    const int k0 = BN * j;
     const bool act = FULL || !CAUSAL || k0 <= qw + 31;
-    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= qw + 31));
+    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - BN <= qw + 31));
     if (act) {
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
 #if FA16_PRIO
       __builtin_amdgcn_s_setprio(1);
 #endif
+      f32x16 sc[KB];
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        s0 = M::mma(kfrag(KST, 0, ks), qf[ks], s0);
-        s1 = M::mma(kfrag(KST, 1, ks), qf[ks], s1);
-      }
+      for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sc[kb] = M::mma(kfrag(KST, kb, ks), qf[ks], sc[kb]);
 #if FA16_SCHED
       // keep FA16_SCHED K-fragment reads in flight ahead of the matrix ops
       __builtin_amdgcn_sched_group_barrier(0x100, FA16_SCHED, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * KSTEPS - FA16_SCHED; ++i) {
+      for (int i = 0; i < KB * KSTEPS - FA16_SCHED; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
@@ -178,24 +195,74 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 #if FA16_PRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
-      const int t0 = lim - k0 - 4 * h, t1 = t0 - 32;
-      float xs[32];
+#if FA16_SPEC
+      if constexpr (FULL) {
+        // Unmasked tile: exponentiate against the running maximum m without
+        // looking for this tile's maximum first. If a lane's partial row sum
+        // stays <= 2^8, every p is <= 2^8, which is the bound the lazy rescale
+        // keeps anyway. Otherwise (rare) redo the tile against the new maximum.
+        pv(KST ^ 1);
+        const float negm = -m;
+        float rs = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ro = 8 * (r >> 2) + (r & 3);
-        float x0 = s0[r], x1 = s1[r];
-        if constexpr (!FULL) {
-          x0 = ro <= t0 ? x0 : -__builtin_inff();
-          x1 = ro <= t1 ? x1 : -__builtin_inff();
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            f32x16 p8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, negm));
+              rs += p8[8 * t + e];
+            }
+            pf[kb][t] = acc_frag<T>(p8, t);
+          }
+        if (any_lane(rs > 256.0f)) {
+          float mx = sc[0][0];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, sc[kb][r]);
+          const float mnew = __builtin_fmaxf(m, halves_max(mx) * c);
+          const float alpha = fast_exp2(m - mnew);
+          rs = 0.0f;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              f32x16 p8;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, -mnew));
+                rs += p8[8 * t + e];
+              }
+              pf[kb][t] = acc_frag<T>(p8, t);
+            }
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+          l *= alpha;
+          m = mnew;
         }
-        xs[2 * r] = x0;
-        xs[2 * r + 1] = x1;
+        l += rs;
+        return;
       }
-      // 3-input max tree: 32 values in 16 v_max3
+#endif
+      // key of register r in block kb is k0 + 32 kb + acc_row(r, h); allowed iff <= lim
+      const int t0 = lim - k0 - 4 * h;
+      float xs[KB * 16];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ro = 8 * (r >> 2) + (r & 3);
+          float x = sc[kb][r];
+          if constexpr (!FULL) x = ro <= t0 - 32 * kb ? x : -__builtin_inff();
+          xs[16 * kb + r] = x;
+        }
+      // 3-input max tree over the lane's scores
       float mx = __builtin_fmaxf(xs[0], __builtin_fmaxf(xs[1], xs[2]));
 #pragma unroll
-      for (int r = 3; r + 1 < 32; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(xs[r], xs[r + 1]));
-      mx = __builtin_fmaxf(mx, xs[31]);
+      for (int r = 3; r + 1 < KB * 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(xs[r], xs[r + 1]));
+      mx = __builtin_fmaxf(mx, xs[KB * 16 - 1]);
       mx = halves_max(mx);
       float mt = mx * c;
       if constexpr (!FULL) mt = mx > -__builtin_inff() ? mt : -__builtin_inff();
@@ -206,18 +273,17 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
       if (prev) pv(KST ^ 1);
       float rs = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p0 = fast_exp2(__builtin_fmaf(s0[r], c, negm));
-        float p1 = fast_exp2(__builtin_fmaf(s1[r], c, negm));
-        if constexpr (!FULL) {
-          const int ro = 8 * (r >> 2) + (r & 3);
-          p0 = ro <= t0 ? p0 : 0.0f;
-          p1 = ro <= t1 ? p1 : 0.0f;
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(sc[kb][r], c, negm));
+          if constexpr (!FULL) {
+            const int ro = 8 * (r >> 2) + (r & 3);
+            p = ro <= t0 - 32 * kb ? p : 0.0f;
+          }
+          sc[kb][r] = p;
+          rs += p;
         }
-        s0[r] = p0;
-        s1[r] = p1;
-        rs += p0 + p1;
-      }
       if (need) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
@@ -226,10 +292,9 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
       l += rs;
       m = mnew;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        pf[0][t] = acc_frag<T>(s0, t);
-        pf[1][t] = acc_frag<T>(s1, t);
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) pf[kb][t] = acc_frag<T>(sc[kb], t);
     } else if (prev) {
       pv(KST ^ 1);
     }
@@ -255,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   // the last tile's P still owes its V product
   wait_vmem();
   __builtin_amdgcn_s_barrier();
-  if (!CAUSAL || 64 * (nt - 1) <= qw + 31) {
+  if (!CAUSAL || BN * (nt - 1) <= qw + 31) {
     if ((nt - 1) & 1)
       pv(1);
     else

@@ -1,6 +1,6 @@
 // fa_tile16.h -- LDS tiles of 16-bit rows filled by direct (buffer -> LDS) loads.
 //
-// A tile is 64 rows of D 16-bit elements, rows packed back to back.  Direct
+// A tile is ROWS (64 by default) rows of D 16-bit elements, rows packed back to back.  Direct
 // loads write 1 KiB per wave instruction, contiguously, so rows cannot be
 // padded; instead the 16-byte chunks of row r are stored XOR-permuted by
 // sw(r).  With sw chosen per row length (checked with a 64-bank model), the
@@ -15,12 +15,12 @@
 
 namespace fa {
 
-template <int D>
+template <int D, int ROWS = 64>
 struct Tile16 {
   static constexpr int ROWB = 2 * D;
-  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row: 8 or 16
-  static constexpr int BYTES = 64 * ROWB;        // 8 KiB or 16 KiB
-  static constexpr int ROUNDS = 64 * CPR / 256;  // direct loads per tile per wave (4 waves)
+  static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row: 8 or 16
+  static constexpr int BYTES = ROWS * ROWB;        // 8, 16 or 32 KiB
+  static constexpr int ROUNDS = ROWS * CPR / 256;  // direct loads per tile per wave (4 waves)
   __device__ static constexpr int sw(int r) {
     return CPR == 16 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
   }
@@ -33,9 +33,9 @@ __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Source offset (bytes inside a tile) each lane loads in direct-load round i,
 // for a 4-wave workgroup: slot s = (4 i + wave) * 64 + lane holds logical
 // chunk (s % CPR) ^ sw(row) of row s / CPR.
-template <int D>
+template <int D, int ROWS = 64>
 __device__ inline void tile16_load_offsets(uint32_t* goff, int wave, int lane) {
-  using TL = Tile16<D>;
+  using TL = Tile16<D, ROWS>;
 #pragma unroll
   for (int i = 0; i < TL::ROUNDS; ++i) {
     const int s = (i * 4 + wave) * 64 + lane;
