@@ -156,3 +156,102 @@ def attention_backward_rows(q, k, v, do, scale, causal, b, h, rows):
         ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
         out[t] = scale * (ds @ kh)[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# Queries and keys of different counts, and padded batches.
+#
+# The pages apply causal masking "for autoregressive decoding" and apply
+# causal masking and padding per tile, with boundary tiles cut by the mask
+# ("How Flash Attention Works: Tiling, Softmax, GPU I/O", sections "How Flash
+# Attention Works: The Exact-Attention Idea" and "Tiling Q, K, and V for Fast
+# On-Chip Memory").  They fix neither the alignment of a causal mask when the
+# query count differs from the key count nor what a padded row outputs; the
+# readings taken here:
+#   * sequence b has lq_b real queries and lk_b real keys (lengths outside
+#     [0, Nq] / [0, Nk] are clamped into them); rows at or past a length are
+#     padding;
+#   * the lq_b queries are the last lq_b positions of the lk_b-key sequence
+#     (decoding with a cache of earlier keys), so under the causal mask query i
+#     sees key j iff j <= i + (lk_b - lq_b);
+#   * a query that sees no key, and every padding row, outputs O = 0 and
+#     LSE = -inf, and contributes nothing to any gradient; padding rows of
+#     dQ, dK and dV are 0.
+# ---------------------------------------------------------------------------
+
+
+def _lengths(lens, B, n):
+    """Per-sequence lengths clamped into [0, n] (all n when lens is None)."""
+    if lens is None:
+        return [n] * B
+    return [min(max(int(x), 0), n) for x in np.asarray(lens).reshape(-1)[:B]]
+
+
+def _scores_kv(q, k, scale, causal, off):
+    """S = scale * q k^T for one sequence; query i may see key j iff j <= i + off (causal)."""
+    s = scale * (q @ k.T)
+    if causal:
+        rows = np.arange(q.shape[0])[:, None] + off
+        cols = np.arange(k.shape[0])[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    return s
+
+
+def _softmax_rows_kv(s):
+    """Row softmax and LSE where a row may have no visible key (P = 0, LSE = -inf)."""
+    n = s.shape[0]
+    if s.shape[1] == 0:
+        return np.zeros_like(s), np.full(n, -np.inf)
+    m = np.max(s, axis=1)
+    seen = np.isfinite(m)
+    m0 = np.where(seen, m, 0.0)[:, None]
+    e = np.exp(s - m0)  # exp(-inf) = 0 for the masked entries
+    l = np.sum(e, axis=1)
+    p = np.zeros_like(e)
+    p[seen] = e[seen] / l[seen, None]
+    lse = np.full(n, -np.inf)
+    lse[seen] = m[seen] + np.log(l[seen])
+    return p, lse
+
+
+def attention_forward_kv(q, k, v, scale, causal, seqlens_q=None, seqlens_k=None):
+    """O and LSE for q [B,H,Nq,d], k and v [B,H,Nk,d] under the readings above.
+
+    Returns (O [B,H,Nq,d] float64, LSE [B,H,Nq] float64, natural log).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, _ = q.shape
+    Nk = k.shape[2]
+    lq, lk = _lengths(seqlens_q, B, Nq), _lengths(seqlens_k, B, Nk)
+    o = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        off = lk[b] - lq[b]
+        for h in range(H):
+            p, lse[b, h, :lq[b]] = _softmax_rows_kv(_scores_kv(q[b, h, :lq[b]], k[b, h, :lk[b]], scale, causal, off))
+            o[b, h, :lq[b]] = p @ v[b, h, :lk[b]]
+    return o, lse
+
+
+def attention_backward_kv(q, k, v, do, scale, causal, seqlens_q=None, seqlens_k=None):
+    """dQ, dK, dV of L = sum(dO * O) for the forward above (float64).
+
+    Per sequence, on its real rows only: dV = P^T dO, dP = dO V^T,
+    D_i = sum_j P_ij dP_ij, dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, Nq, _ = q.shape
+    Nk = k.shape[2]
+    lq, lk = _lengths(seqlens_q, B, Nq), _lengths(seqlens_k, B, Nk)
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        a, c, off = lq[b], lk[b], lk[b] - lq[b]
+        for h in range(H):
+            qh, kh, vh, doh = q[b, h, :a], k[b, h, :c], v[b, h, :c], do[b, h, :a]
+            p, _ = _softmax_rows_kv(_scores_kv(qh, kh, scale, causal, off))
+            dv[b, h, :c] = p.T @ doh
+            dp = doh @ vh.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h, :a] = scale * (ds @ kh)
+            dk[b, h, :c] = scale * (ds.T @ qh)
+    return dq, dk, dv

@@ -283,7 +283,203 @@ def pin_backward_invariants(orc):
             _close(g, np.zeros_like(g), 0.0, "dO = 0 gives zero gradients")
 
 
+# ------------------------------------------- unequal counts, padded batches
+# Readings (the pages fix neither): the lq queries of a sequence are the last
+# lq positions of its lk keys, so under the causal mask query i sees key j iff
+# j <= i + (lk - lq); rows past a length, and rows that see no key, output
+# O = 0 and LSE = -inf and take no part in any gradient.
+def _visible(i, j, lq, lk, causal):
+    return i < lq and j < lk and (not causal or j <= i + (lk - lq))
+
+
+def _brute_kv(q, k, v, scale, causal, lq, lk):
+    """One (b, h) slice by scalar loops: O [Nq][dv] and LSE [Nq]."""
+    nq, dv = len(q), len(v[0])
+    o = [[0.0] * dv for _ in range(nq)]
+    lse = [-math.inf] * nq
+    for i in range(nq):
+        js = [j for j in range(len(k)) if _visible(i, j, lq, lk, causal)]
+        if not js:
+            continue
+        s = {j: scale * math.fsum(a * b for a, b in zip(q[i], k[j])) for j in js}
+        m = max(s.values())
+        w = {j: math.exp(s[j] - m) for j in js}
+        z = math.fsum(w.values())
+        lse[i] = m + math.log(z)
+        for c in range(dv):
+            o[i][c] = math.fsum(w[j] * v[j][c] for j in js) / z
+    return o, lse
+
+
+def _qkv_kv(seed, B, H, Nq, Nk, d):
+    r = _rng(seed)
+    return r.standard_normal((B, H, Nq, d)), r.standard_normal((B, H, Nk, d)), r.standard_normal((B, H, Nk, d))
+
+
+def pin_kv_reduces_to_square(orc):
+    """Equal counts and no lengths give the square definition exactly."""
+    q, k, v = _qkv(30, 2, 2, 19, 8)
+    do = _rng(31).standard_normal(q.shape)
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.3, causal)
+        o2, lse2 = orc.attention_forward_kv(q, k, v, 0.3, causal, [19, 19], None)
+        _close(o2, o, 1e-13, f"kv O = square O causal={causal}")
+        _close(lse2, lse, 1e-13, f"kv LSE = square LSE causal={causal}")
+        g = orc.attention_backward(q, k, v, do, 0.3, causal)
+        g2 = orc.attention_backward_kv(q, k, v, do, 0.3, causal)
+        for a, b, n in zip(g2, g, "QKV"):
+            _close(a, b, 1e-12, f"kv d{n} = square d{n} causal={causal}")
+
+
+def pin_kv_worked_example(orc):
+    with open(os.path.join(GOLDEN, "kv_worked_example.json")) as f:
+        g = json.load(f)
+    q, k, v, do = (_mat(g[n])[None, None] for n in ("q", "k", "v", "do"))
+    pad = g["padded"]
+    qp = np.concatenate([q, _mat([pad["q_pad_row"]])[None, None]], axis=2)
+    kp = np.concatenate([k, _mat([pad["k_pad_row"]])[None, None]], axis=2)
+    vp = np.concatenate([v, _mat([pad["v_pad_row"]])[None, None]], axis=2)
+    dop = np.concatenate([do, _mat([pad["do_pad_row"]])[None, None]], axis=2)
+    for mode, causal in (("noncausal", False), ("causal", True)):
+        e = g[mode]
+        want = {n: _mat(e[n]) for n in ("o", "dq", "dk", "dv")}
+        want_lse = [_ev(x) for x in e["lse"]]
+        o, lse = orc.attention_forward_kv(q, k, v, g["scale"], causal)
+        _close(o[0, 0], want["o"], 1e-14, f"kv worked O {mode}")
+        _close(lse[0, 0], want_lse, 1e-14, f"kv worked LSE {mode}")
+        dq, dk, dv = orc.attention_backward_kv(q, k, v, do, g["scale"], causal)
+        _close(dq[0, 0], want["dq"], 1e-14, f"kv worked dQ {mode}")
+        _close(dk[0, 0], want["dk"], 1e-14, f"kv worked dK {mode}")
+        _close(dv[0, 0], want["dv"], 1e-14, f"kv worked dV {mode}")
+        # padded to 3 query rows / 4 key rows, lengths (2, 3): same values, zero padding rows
+        o, lse = orc.attention_forward_kv(qp, kp, vp, g["scale"], causal, pad["seqlens_q"], pad["seqlens_k"])
+        _close(o[0, 0], np.vstack([want["o"], np.zeros((1, 2))]), 1e-14, f"kv padded O {mode}")
+        assert lse[0, 0, 2] == -math.inf, f"kv padded LSE row {mode}"
+        _close(lse[0, 0, :2], want_lse, 1e-14, f"kv padded LSE {mode}")
+        dq, dk, dv = orc.attention_backward_kv(qp, kp, vp, dop, g["scale"], causal, pad["seqlens_q"], pad["seqlens_k"])
+        _close(dq[0, 0], np.vstack([want["dq"], np.zeros((1, 1))]), 1e-14, f"kv padded dQ {mode}")
+        _close(dk[0, 0], np.vstack([want["dk"], np.zeros((1, 1))]), 1e-14, f"kv padded dK {mode}")
+        _close(dv[0, 0], np.vstack([want["dv"], np.zeros((1, 2))]), 1e-14, f"kv padded dV {mode}")
+
+
+def pin_kv_bruteforce(orc):
+    """Ragged lengths, both alignments of counts, rows that see no key."""
+    q, k, v = _qkv_kv(32, 3, 2, 6, 5, 3)
+    lens = ([6, 4, 2], [5, 5, 3])  # lq > lk (empty causal rows), lq < lk, lq < lk
+    for causal in (False, True):
+        for scale in (0.7, -0.4):
+            o, lse = orc.attention_forward_kv(q, k, v, scale, causal, *lens)
+            for b in range(3):
+                for h in range(2):
+                    bo, bl = _brute_kv(q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist(), scale, causal,
+                                       lens[0][b], lens[1][b])
+                    _close(o[b, h], bo, 1e-12, f"kv brute O b={b} causal={causal}")
+                    assert np.array_equal(np.isinf(lse[b, h]), np.isinf(bl)), f"kv brute empty rows b={b}"
+                    fin = ~np.isinf(np.asarray(bl))
+                    _close(lse[b, h][fin], np.asarray(bl)[fin], 1e-12, f"kv brute LSE b={b} causal={causal}")
+
+
+def pin_kv_decode_and_empty(orc):
+    q, k, v = _qkv_kv(33, 2, 2, 1, 9, 4)
+    # one query at the end of the sequence sees every key: causal = non-causal
+    oc, lc = orc.attention_forward_kv(q, k, v, 0.5, True)
+    on, ln_ = orc.attention_forward_kv(q, k, v, 0.5, False)
+    _close(oc, on, 1e-15, "decode causal = non-causal")
+    _close(lc, ln_, 1e-15, "decode LSE")
+    # three queries, one key, causal: rows 0 and 1 see nothing; row 2 sees key 0 only
+    q, k, v = _qkv_kv(34, 1, 1, 3, 1, 4)
+    o, lse = orc.attention_forward_kv(q, k, v, 0.5, True)
+    _close(o[0, 0, :2], np.zeros((2, 4)), 0.0, "empty rows O = 0")
+    assert np.all(lse[0, 0, :2] == -math.inf), "empty rows LSE = -inf"
+    _close(o[0, 0, 2], v[0, 0, 0], 1e-15, "single visible key: O = v_0")
+    _close(lse[0, 0, 2], 0.5 * float(q[0, 0, 2] @ k[0, 0, 0]), 1e-15, "single visible key: LSE = s")
+    do = _rng(35).standard_normal(q.shape)
+    dq, dk, dv = orc.attention_backward_kv(q, k, v, do, 0.5, True)
+    _close(dq[0, 0], np.zeros((3, 4)), 0.0, "one key: dS = 0 so dQ = 0")
+    _close(dk[0, 0], np.zeros((1, 4)), 0.0, "one key: dK = 0")
+    _close(dv[0, 0, 0], do[0, 0, 2], 1e-15, "one key: dV_0 = dO of the row that sees it")
+    # no keys at all
+    o, lse = orc.attention_forward_kv(q, k, v, 0.5, False, None, [0])
+    _close(o, np.zeros_like(o), 0.0, "lk = 0: O = 0")
+    assert np.all(lse == -math.inf), "lk = 0: LSE = -inf"
+
+
+def pin_kv_padding_invariance(orc):
+    """Values past the lengths change nothing; lengths outside [0, N] are clamped."""
+    q, k, v = _qkv_kv(36, 2, 2, 7, 8, 4)
+    do = _rng(37).standard_normal(q.shape)
+    lq, lk = [5, 7], [8, 3]
+    q2, k2, v2, do2 = q.copy(), k.copy(), v.copy(), do.copy()
+    q2[0, :, 5:] = 9.0; do2[0, :, 5:] = -3.0
+    k2[1, :, 3:] = 7.0; v2[1, :, 3:] = 5.0
+    for causal in (False, True):
+        a = orc.attention_forward_kv(q, k, v, 0.4, causal, lq, lk)
+        b = orc.attention_forward_kv(q2, k2, v2, 0.4, causal, lq, lk)
+        for x, y, n in zip(a, b, ("O", "LSE")):
+            assert np.array_equal(x, y), f"padding values leak into {n} causal={causal}"
+        assert np.all(a[0][0, :, 5:] == 0) and np.all(a[1][0, :, 5:] == -math.inf), "padding rows"
+        ga = orc.attention_backward_kv(q, k, v, do, 0.4, causal, lq, lk)
+        gb = orc.attention_backward_kv(q2, k2, v2, do2, 0.4, causal, lq, lk)
+        for x, y, n in zip(ga, gb, "QKV"):
+            assert np.array_equal(x, y), f"padding values leak into d{n} causal={causal}"
+        assert np.all(ga[0][0, :, 5:] == 0) and np.all(ga[1][1, :, 3:] == 0) and np.all(ga[2][1, :, 3:] == 0)
+        c = orc.attention_forward_kv(q, k, v, 0.4, causal, [99, 5], [8, -4])
+        d = orc.attention_forward_kv(q, k, v, 0.4, causal, [7, 5], [8, 0])
+        assert np.array_equal(c[0], d[0]) and np.array_equal(c[1], d[1]), "lengths are clamped into [0, N]"
+
+
+def pin_kv_torch_autograd(orc):
+    """Per sequence: torch float64 autograd of the naive expression with an explicit mask."""
+    import torch
+    q, k, v = _qkv_kv(38, 2, 2, 6, 9, 5)
+    do = _rng(39).standard_normal(q.shape)
+    lq, lk = [6, 4], [9, 7]
+    for causal in (False, True):
+        o, lse = orc.attention_forward_kv(q, k, v, 0.35, causal, lq, lk)
+        dq, dk, dv = orc.attention_backward_kv(q, k, v, do, 0.35, causal, lq, lk)
+        for b in range(2):
+            a, c = lq[b], lk[b]
+            tq, tk, tv = (torch.tensor(x[b, :, :n], dtype=torch.float64, requires_grad=True)
+                          for x, n in ((q, a), (k, c), (v, c)))
+            s = 0.35 * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+            if causal:
+                i = torch.arange(a)[:, None] + (c - a)
+                j = torch.arange(c)[None, :]
+                s = s.masked_fill(j > i, float("-inf"))
+            out = torch.matmul(torch.softmax(s, dim=-1), tv)
+            (out * torch.tensor(do[b, :, :a])).sum().backward()
+            _close(o[b, :, :a], out.detach().numpy(), 1e-12, f"kv autograd O b={b} causal={causal}")
+            _close(lse[b, :, :a], torch.logsumexp(s, dim=-1).detach().numpy(), 1e-12, f"kv autograd LSE b={b}")
+            _close(dq[b, :, :a], tq.grad.numpy(), 1e-10, f"kv autograd dQ b={b} causal={causal}")
+            _close(dk[b, :, :c], tk.grad.numpy(), 1e-10, f"kv autograd dK b={b} causal={causal}")
+            _close(dv[b, :, :c], tv.grad.numpy(), 1e-10, f"kv autograd dV b={b} causal={causal}")
+
+
+def pin_kv_finite_differences(orc):
+    q, k, v = _qkv_kv(40, 1, 1, 4, 5, 3)
+    do = _rng(41).standard_normal(q.shape)
+    lq, lk = [3], [4]
+    for causal in (False, True):
+        grads = orc.attention_backward_kv(q, k, v, do, 0.45, causal, lq, lk)
+        base = [q, k, v]
+        h = 1e-6
+        for which in range(3):
+            num = np.zeros_like(base[which])
+            for idx in np.ndindex(base[which].shape):
+                loss = []
+                for sgn in (1.0, -1.0):
+                    xs = [x.copy() for x in base]
+                    xs[which][idx] += sgn * h
+                    o, _ = orc.attention_forward_kv(*xs, 0.45, causal, lq, lk)
+                    loss.append(np.sum(o * do))
+                num[idx] = (loss[0] - loss[1]) / (2 * h)
+            err = np.max(np.abs(num - grads[which])) / max(1.0, np.max(np.abs(num)))
+            assert err < 1e-7, f"kv finite differences grad {which} causal={causal}: {err:.2e}"
+
+
 ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pin_constant_v,
             pin_q_zero, pin_causal_row0_and_n1, pin_shift_invariance, pin_permutation,
             pin_online_recurrence, pin_scipy_logsumexp, pin_torch_autograd,
-            pin_finite_differences, pin_backward_invariants]
+            pin_finite_differences, pin_backward_invariants,
+            pin_kv_reduces_to_square, pin_kv_worked_example, pin_kv_bruteforce, pin_kv_decode_and_empty,
+            pin_kv_padding_invariance, pin_kv_torch_autograd, pin_kv_finite_differences]

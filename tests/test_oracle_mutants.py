@@ -32,6 +32,18 @@ MUTANTS = {
     "dK sign": ("dk = scale * (ds.T @ q)", "dk = -scale * (ds.T @ q)"),
     "dQ uses V": ("dq = scale * (ds @ k)", "dq = scale * (ds @ v)"),
     "output uses K": ("o[r0:r1] = p @ v", "o[r0:r1] = p @ k"),
+    # unequal counts and padded batches
+    "kv top-left alignment": ("rows = np.arange(q.shape[0])[:, None] + off", "rows = np.arange(q.shape[0])[:, None]"),
+    "kv offset sign (forward)": ("off = lk[b] - lq[b]", "off = lq[b] - lk[b]"),
+    "kv offset sign (backward)": ("a, c, off = lq[b], lk[b], lk[b] - lq[b]", "a, c, off = lq[b], lk[b], lq[b] - lk[b]"),
+    "kv key lengths ignored": ("lq, lk = _lengths(seqlens_q, B, Nq), _lengths(seqlens_k, B, Nk)",
+                               "lq, lk = _lengths(seqlens_q, B, Nq), _lengths(None, B, Nk)"),
+    "kv lengths not clamped": ("return [min(max(int(x), 0), n) for x", "return [int(x) for x"),
+    "kv padding rows not zero": ("o = np.zeros(q.shape[:3] + (v.shape[3],))", "o = np.ones(q.shape[:3] + (v.shape[3],))"),
+    "kv empty rows weighted": ("p[seen] = e[seen] / l[seen, None]", "p = e / np.maximum(l, 1e-300)[:, None] + (~seen)[:, None]"),
+    "kv dQ missing scale": ("dq[b, h, :a] = scale * (ds @ kh)", "dq[b, h, :a] = (ds @ kh)"),
+    "kv dropped D term": ("ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))\n            dq[b, h, :a]",
+                          "ds = p * dp\n            dq[b, h, :a]"),
 }
 
 
