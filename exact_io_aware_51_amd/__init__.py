@@ -1,12 +1,13 @@
 """Python binding of libfa, the gfx950 fused exact-attention library.
 
-The functions named like the C entry points (fa_fwd, fa_bwd,
-fa_bwd_workspace_bytes, fa_status_string, fa_version) take raw device
-addresses and sizes exactly as include/fa.h declares them.  forward() and
-backward() are conveniences for torch tensors: they check shapes, allocate the
-outputs with torch, pass data_ptr()s and torch's current HIP stream, and raise
-FaError on a non-zero status.  All arithmetic happens in the HIP kernels; there
-is no CPU or PyTorch fallback, and a missing library is an error.
+The functions named like the C entry points (fa_fwd, fa_bwd, fa_fwd_kv,
+fa_bwd_kv, fa_bwd_workspace_bytes, fa_status_string, fa_version, ...) take raw
+device addresses and sizes exactly as include/fa.h declares them.  forward(),
+backward(), forward_kv() and backward_kv() are conveniences for torch tensors:
+they check shapes, allocate the outputs with torch, pass data_ptr()s and
+torch's current HIP stream, and raise FaError on a non-zero status.  All
+arithmetic happens in the HIP kernels; there is no CPU or PyTorch fallback,
+and a missing library is an error.
 """
 from __future__ import annotations
 
@@ -15,8 +16,8 @@ import math
 import os
 
 __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_status_string", "fa_version",
-           "forward", "backward", "library_path", "load"]
+           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_status_string",
+           "fa_version", "forward", "backward", "forward_kv", "backward_kv", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
@@ -25,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_status_string", "fa_version")
+           "fa_fwd_kv", "fa_bwd_kv", "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -59,6 +60,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_dq.restype = i
+    lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i, i, vp]
+    lib.fa_fwd_kv.restype = i
+    lib.fa_bwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, vp, vp, f, i, i, vp]
+    lib.fa_bwd_kv.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -94,6 +99,16 @@ def fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, sc
               stream) -> int:
     return load().fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, scale, causal,
                             dtype, stream)
+
+
+def fa_fwd_kv(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, dtype, stream) -> int:
+    return load().fa_fwd_kv(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, dtype, stream)
+
+
+def fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, d, seqlens_q,
+              seqlens_k, scale, causal, dtype, stream) -> int:
+    return load().fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, d,
+                            seqlens_q, seqlens_k, scale, causal, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
@@ -171,4 +186,72 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, st
                 B, H, N, d, scale, int(bool(causal)), code, _stream(q, stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _check_kv(q, k, v, extra_q=(), extra_k=()):
+    import torch
+    for t in (q, k, v, *extra_q, *extra_k):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError("tensors must live on a HIP device (no CPU path exists)")
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("expected contiguous [B, H, N, d] tensors of one dtype and device")
+    B, H, Nq, d = q.shape
+    for t in (k, v, *extra_k):
+        if t.shape[:2] != (B, H) or t.shape[3] != d or t.shape[2] != k.shape[2]:
+            raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    for t in extra_q:
+        if t.shape != q.shape:
+            raise ValueError("o and dout must have q's shape")
+    return B, H, Nq, k.shape[2], d
+
+
+def _lengths(t, B, device):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        t = torch.tensor(list(t), dtype=torch.int32, device=device)
+    if t.device != device or t.dtype != torch.int32 or t.numel() != B or not t.is_contiguous():
+        raise ValueError("sequence lengths must be a contiguous int32 device tensor of B entries")
+    return t
+
+
+def forward_kv(q, k, v, seqlens_q=None, seqlens_k=None, scale=None, causal=False, need_lse=True, stream=None):
+    """fa_fwd_kv on torch tensors: q [B,H,Nq,d], k/v [B,H,Nk,d], optional per-sequence lengths.
+
+    Under the causal mask the queries are the last positions of their key sequence
+    (query i sees key j iff j <= i + lk - lq); padding rows get O = 0, LSE = -inf.
+    """
+    import torch
+    B, H, Nq, Nk, d = _check_kv(q, k, v)
+    sq, sk = _lengths(seqlens_q, B, q.device), _lengths(seqlens_k, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if need_lse else None
+    st = fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                   lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d,
+                   sq.data_ptr() if sq is not None else None, sk.data_ptr() if sk is not None else None,
+                   scale, int(bool(causal)), _dtype_code(q), _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_kv")
+    return o, lse
+
+
+def backward_kv(q, k, v, o, lse, dout, seqlens_q=None, seqlens_k=None, scale=None, causal=False, stream=None):
+    """fa_bwd_kv on torch tensors (o and lse from forward_kv with the same arguments)."""
+    import torch
+    B, H, Nq, Nk, d = _check_kv(q, k, v, extra_q=(o, dout))
+    sq, sk = _lengths(seqlens_q, B, q.device), _lengths(seqlens_k, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_bytes(B, H, Nq, d, code)
+    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                   B, H, Nq, Nk, d, sq.data_ptr() if sq is not None else None,
+                   sk.data_ptr() if sk is not None else None, scale, int(bool(causal)), code, _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_kv")
     return dq, dk, dv

@@ -29,17 +29,51 @@ bool overlap(Range a, Range b) {
 size_t elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
 // Shape / dtype / scale checks shared by both passes.
-int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
+int check_shape(int B, int H, int Nq, int Nk, int d, float scale, int causal, int dtype) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
-  if ((long long)B * H * N >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * Nq >= (1LL << 31) || (long long)B * H * Nk >= (1LL << 31)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !std::isfinite(scale * 1.4426950408889634f)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
+  return check_shape(B, H, N, N, d, scale, causal, dtype);
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// Forward validation and launch for q/o of Nq rows and k/v of Nk rows per
+// (batch, head), with optional device arrays of per-sequence lengths.
+int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+            const int* seqlens_q, const int* seqlens_k, float scale, int causal, int dtype, void* stream) {
+  int st = check_shape(B, H, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  if ((seqlens_q && !aligned(seqlens_q, 4)) || (seqlens_k && !aligned(seqlens_k, 4))) return FA_ERR_INVALID_ARG;
+  const size_t tq = (size_t)B * H * Nq * d * elem_bytes(dtype);
+  const size_t tk = (size_t)B * H * Nk * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * Nq * sizeof(float);
+  const size_t sb = (size_t)B * sizeof(int);
+  const Range ins[5] = {{q, tq}, {k, tk}, {v, tk}, {seqlens_q, seqlens_q ? sb : 0}, {seqlens_k, seqlens_k ? sb : 0}};
+  for (const Range& r : ins) {
+    if (overlap({o, tq}, r)) return FA_ERR_INVALID_ARG;
+    if (lse && overlap({lse, lb}, r)) return FA_ERR_INVALID_ARG;
+  }
+  if (lse && overlap({o, tq}, {lse, lb})) return FA_ERR_INVALID_ARG;
+
+  fa::FwdProblem p;
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk; p.d = d;
+  p.seqlens_q = seqlens_q; p.seqlens_k = seqlens_k;
+  p.scale = scale; p.causal = causal; p.dtype = dtype;
+  (void)hipGetLastError();  // report only this launch's error
+  return hip_status(fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream)));
+}
 
 }  // namespace
 
@@ -60,26 +94,12 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, fa_dtype dtype, void* stream) {
-  int st = check_common(B, H, N, d, scale, causal, (int)dtype);
-  if (st != FA_OK) return st;
-  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
-  if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
-  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const Range ins[3] = {{q, tb}, {k, tb}, {v, tb}};
-  for (const Range& r : ins) {
-    if (overlap({o, tb}, r)) return FA_ERR_INVALID_ARG;
-    if (lse && overlap({lse, lb}, r)) return FA_ERR_INVALID_ARG;
-  }
-  if (lse && overlap({o, tb}, {lse, lb})) return FA_ERR_INVALID_ARG;
+  return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype, stream);
+}
 
-  fa::FwdProblem p;
-  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-  p.B = B; p.H = H; p.N = N; p.d = d;
-  p.scale = scale; p.causal = causal; p.dtype = (int)dtype;
-  (void)hipGetLastError();  // report only this launch's error
-  return hip_status(fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream)));
+int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
+              const int* seqlens_q, const int* seqlens_k, float scale, int causal, fa_dtype dtype, void* stream) {
+  return run_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, (int)dtype, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
@@ -103,22 +123,26 @@ struct BwdPtrs {
 const char kUnusedTag = 0;
 const void* const kUnused = &kUnusedTag;
 
-int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-              int dtype) {
-  int st = check_common(B, H, N, d, scale, causal, dtype);
+int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, const int* seqlens_q,
+              const int* seqlens_k, float scale, int causal, int dtype) {
+  int st = check_shape(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
+  if ((seqlens_q && !aligned(seqlens_q, 4)) || (seqlens_k && !aligned(seqlens_k, 4))) return FA_ERR_INVALID_ARG;
   const void* p16[] = {p.q, p.k, p.v, p.o, p.dout, p.dq, p.dk, p.dv};
   for (const void* x : p16) {
     if (x == kUnused) continue;
     if (!x || !aligned(x, 16)) return FA_ERR_INVALID_ARG;
   }
   if (p.lse != kUnused && (!p.lse || !aligned(p.lse, 4))) return FA_ERR_INVALID_ARG;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, (fa_dtype)dtype);
+  const size_t need = fa_bwd_workspace_bytes(B, H, Nq, d, (fa_dtype)dtype);
   if (!p.ws || workspace_bytes < need || !aligned(p.ws, 16)) return FA_ERR_WORKSPACE;
-  const size_t tb = (size_t)B * H * N * d * elem_bytes(dtype);
-  const size_t lb = (size_t)B * H * N * sizeof(float);
-  const Range ins[6] = {{p.q, tb}, {p.k, tb}, {p.v, tb}, {p.o, tb}, {p.dout, tb}, {p.lse, lb}};
-  const Range outs[4] = {{p.dq, tb}, {p.dk, tb}, {p.dv, tb}, {p.ws, need}};
+  const size_t tq = (size_t)B * H * Nq * d * elem_bytes(dtype);
+  const size_t tk = (size_t)B * H * Nk * d * elem_bytes(dtype);
+  const size_t lb = (size_t)B * H * Nq * sizeof(float);
+  const size_t sb = (size_t)B * sizeof(int);
+  const Range ins[8] = {{p.q, tq},    {p.k, tk},   {p.v, tk}, {p.o, tq}, {p.dout, tq}, {p.lse, lb},
+                        {seqlens_q ? seqlens_q : kUnused, sb}, {seqlens_k ? seqlens_k : kUnused, sb}};
+  const Range outs[4] = {{p.dq, tq}, {p.dk, tk}, {p.dv, tk}, {p.ws, need}};
   for (int i = 0; i < 4; ++i) {
     if (outs[i].p == kUnused) continue;
     for (const Range& r : ins)
@@ -129,14 +153,16 @@ int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int N, int
   return FA_OK;
 }
 
-fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int N, int d, float scale, int causal, int dtype) {
+fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d, const int* seqlens_q,
+                          const int* seqlens_k, float scale, int causal, int dtype) {
   fa::BwdProblem b;
   auto use = [](const void* x) { return x == kUnused ? nullptr : x; };
   b.q = use(p.q); b.k = use(p.k); b.v = use(p.v); b.o = use(p.o); b.dout = use(p.dout);
   b.lse = static_cast<const float*>(use(p.lse));
   b.dq = const_cast<void*>(use(p.dq)); b.dk = const_cast<void*>(use(p.dk)); b.dv = const_cast<void*>(use(p.dv));
   b.dvec = static_cast<float*>(p.ws);
-  b.B = B; b.H = H; b.N = N; b.d = d;
+  b.B = B; b.H = H; b.Nq = Nq; b.Nk = Nk; b.d = d;
+  b.seqlens_q = seqlens_q; b.seqlens_k = seqlens_k;
   b.scale = scale; b.causal = causal; b.dtype = dtype;
   return b;
 }
@@ -156,18 +182,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, fa_dtype dtype, void* stream) {
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
-  int st = check_bwd(p, workspace_bytes, B, H, N, d, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, d, scale, causal, (int)dtype), 0, 2, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype), 0, 2, stream);
+}
+
+int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk,
+              int d, const int* seqlens_q, const int* seqlens_k, float scale, int causal, fa_dtype dtype,
+              void* stream) {
+  const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  int st = check_bwd(p, workspace_bytes, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, (int)dtype), 0, 2, stream);
 }
 
 int fa_bwd_rowsum(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B, int H, int N,
                   int d, fa_dtype dtype, void* stream) {
   void* un = const_cast<void*>(kUnused);
   const BwdPtrs p{kUnused, kUnused, kUnused, o, dout, kUnused, un, un, un, workspace};
-  int st = check_bwd(p, workspace_bytes, B, H, N, d, 1.0f, 0, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, 1.0f, 0, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, d, 1.0f, 0, (int)dtype), 0, 0, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, 1.0f, 0, (int)dtype), 0, 0, stream);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -175,9 +211,9 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
                 float scale, int causal, fa_dtype dtype, void* stream) {
   void* un = const_cast<void*>(kUnused);
   const BwdPtrs p{q, k, v, kUnused, dout, lse, un, dk, dv, const_cast<void*>(workspace)};
-  int st = check_bwd(p, workspace_bytes, B, H, N, d, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, d, scale, causal, (int)dtype), 1, 1, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype), 1, 1, stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, const void* workspace,
@@ -185,9 +221,9 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
               void* stream) {
   void* un = const_cast<void*>(kUnused);
   const BwdPtrs p{q, k, v, kUnused, dout, lse, dq, un, un, const_cast<void*>(workspace)};
-  int st = check_bwd(p, workspace_bytes, B, H, N, d, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, d, scale, causal, (int)dtype), 2, 2, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype), 2, 2, stream);
 }
 
 }  // extern "C"

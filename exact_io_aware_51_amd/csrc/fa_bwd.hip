@@ -34,7 +34,9 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dvec;
-  int N;
+  const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
+  const int* seqlens_k;
+  int Nq, Nk, H;
   int nblk;    // blocks per head along the owned dimension
   int total;   // workgroups in the grid
   float c;     // scale * log2(e), signed
@@ -102,20 +104,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);  // wave-uniform: keep scalar
   const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   const int kb0 = kblk * kBwdOwn;
   const int kw = kb0 + 32 * wave;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
-  const T* __restrict__ Kp = reinterpret_cast<const T*>(a.k) + head;
-  const T* __restrict__ Vp = reinterpret_cast<const T*>(a.v) + head;
-  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + head;
-  const float* __restrict__ lse = a.lse + (size_t)bh * N;
-  const float* __restrict__ dvec = a.dvec + (size_t)bh * N;
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const size_t headq = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + headq;
+  const T* __restrict__ Kp = reinterpret_cast<const T*>(a.k) + headk;
+  const T* __restrict__ Vp = reinterpret_cast<const T*>(a.v) + headk;
+  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + headq;
+  const float* __restrict__ lse = a.lse + (size_t)bh * Nq;
+  const float* __restrict__ dvec = a.dvec + (size_t)bh * Nq;
 
   // K and V rows of this lane's key column, as B fragments (k = d).
   Frag kf[KSTEPS], vf[KSTEPS];
@@ -123,13 +126,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int key = kw + col;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      kf[ks] = key < N ? row_frag<T>(Kp + (size_t)key * D + ks * M::KS, h) : zero_frag<T>();
-      vf[ks] = key < N ? row_frag<T>(Vp + (size_t)key * D + ks * M::KS, h) : zero_frag<T>();
+      kf[ks] = key < sq.lk ? row_frag<T>(Kp + (size_t)key * D + ks * M::KS, h) : zero_frag<T>();
+      vf[ks] = key < sq.lk ? row_frag<T>(Vp + (size_t)key * D + ks * M::KS, h) : zero_frag<T>();
     }
   }
 
-  const int ntiles = (N + kBwdTile - 1) / kBwdTile;
-  const int first = CAUSAL ? kb0 / kBwdTile : 0;
+  // query tiles: real queries only; under the causal mask key j is first seen
+  // by query j - off.  A block of padding keys visits none.
+  const int ntiles = kb0 < sq.lk ? (sq.lq + kBwdTile - 1) / kBwdTile : 0;
+  int first = 0;
+  if (CAUSAL) {
+    const int f = floor_div(kb0 - sq.off, kBwdTile);
+    first = f > 0 ? f : 0;
+  }
 
   u32x4 qreg[L::PER_THREAD], doreg[L::PER_THREAD];
   float lse_r = 0.0f, d_r = 0.0f;
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const int c = tid + i * kBwdThreads;
       const int row = c / L::CPR, cc = c - row * L::CPR;
       const int qi = i0 + row;
-      if (qi < N) {
+      if (qi < sq.lq) {
         const size_t off = (size_t)qi * D + cc * (16 / sizeof(T));
         qreg[i] = *reinterpret_cast<const u32x4*>(Q + off);
         doreg[i] = *reinterpret_cast<const u32x4*>(dO + off);
@@ -151,8 +160,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     if (tid < kBwdTile) {
       const int qi = i0 + tid;
-      lse_r = qi < N ? lse[qi] * kLog2e : 0.0f;
-      d_r = qi < N ? dvec[qi] : 0.0f;
+      lse_r = qi < sq.lq ? lse[qi] * kLog2e : 0.0f;
+      d_r = qi < sq.lq ? dvec[qi] : 0.0f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -190,12 +199,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (j + 1 < ntiles) load_tile(j + 1);
     const int i0 = j * kBwdTile;
     // waves whose keys all follow this tile's last query have nothing to do
-    if (!CAUSAL || i0 + kBwdTile - 1 >= kw) {
+    if (!CAUSAL || i0 + kBwdTile - 1 + sq.off >= kw) {
       const T* qt = lds_q + buf * L::TILE;
       const T* dot = lds_do + buf * L::TILE;
       const float* lt = lds_lse + buf * kBwdTile;
       const float* dt = lds_d + buf * kBwdTile;
-      const bool edge = (i0 + kBwdTile > N) || (CAUSAL && i0 < kw + 31);
+      const bool edge = (i0 + kBwdTile > sq.lq) || (CAUSAL && i0 + sq.off < kw + 31);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
             float p = fast_exp2(__builtin_fmaf(s[r], c, -l4[u]));
             if (edge) {
               const int qi = i0 + rr + u;
-              const bool ok = qi < N && (!CAUSAL || mykey <= qi);
+              const bool ok = qi < sq.lq && (!CAUSAL || mykey <= qi + sq.off);
               p = ok ? p : 0.0f;
             }
             s[r] = p;
@@ -242,18 +251,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (mykey < N) {
-    T* dkrow = reinterpret_cast<T*>(a.dk) + head + (size_t)mykey * D;
-    T* dvrow = reinterpret_cast<T*>(a.dv) + head + (size_t)mykey * D;
+  if (mykey < Nk) {  // padding keys store zeros
+    T* dkrow = reinterpret_cast<T*>(a.dk) + headk + (size_t)mykey * D;
+    T* dvrow = reinterpret_cast<T*>(a.dv) + headk + (size_t)mykey * D;
+    const bool real = mykey < sq.lk;
     const float sc = a.scale;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * h;
-        store4<T>(dkrow + d0, dkacc[mb][4 * g] * sc, dkacc[mb][4 * g + 1] * sc, dkacc[mb][4 * g + 2] * sc,
-                  dkacc[mb][4 * g + 3] * sc);
-        store4<T>(dvrow + d0, dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2], dvacc[mb][4 * g + 3]);
+        float k4[4], v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          k4[u] = real ? dkacc[mb][4 * g + u] * sc : 0.0f;
+          v4[u] = real ? dvacc[mb][4 * g + u] : 0.0f;
+        }
+        store4<T>(dkrow + d0, k4[0], k4[1], k4[2], k4[3]);
+        store4<T>(dvrow + d0, v4[0], v4[1], v4[2], v4[3]);
       }
   }
 }
@@ -276,7 +291,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);  // wave-uniform: keep scalar
@@ -284,28 +299,27 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   if (CAUSAL) qb = a.nblk - 1 - qb;
   const int q0 = qb * kBwdOwn;
   const int qw = q0 + 32 * wave;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
-  const T* __restrict__ Kp = reinterpret_cast<const T*>(a.k) + head;
-  const T* __restrict__ Vp = reinterpret_cast<const T*>(a.v) + head;
-  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + head;
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const size_t headq = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + headq;
+  const T* __restrict__ Kp = reinterpret_cast<const T*>(a.k) + headk;
+  const T* __restrict__ Vp = reinterpret_cast<const T*>(a.v) + headk;
+  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + headq;
 
   const int myq = qw + col;
   Frag qf[KSTEPS], dof[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
-    dof[ks] = myq < N ? row_frag<T>(dO + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
+    qf[ks] = myq < sq.lq ? row_frag<T>(Q + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
+    dof[ks] = myq < sq.lq ? row_frag<T>(dO + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
   }
-  const float lse2 = myq < N ? a.lse[(size_t)bh * N + myq] * kLog2e : 0.0f;
-  const float dq_d = myq < N ? a.dvec[(size_t)bh * N + myq] : 0.0f;
+  const float lse2 = myq < sq.lq ? a.lse[(size_t)bh * Nq + myq] * kLog2e : 0.0f;
+  const float dq_d = myq < sq.lq ? a.dvec[(size_t)bh * Nq + myq] : 0.0f;
 
-  const int ntiles_all = (N + kBwdTile - 1) / kBwdTile;
-  int ntiles = ntiles_all;
-  if (CAUSAL) {
-    const int last = (q0 + kBwdOwn - 1) / kBwdTile + 1;
-    ntiles = last < ntiles_all ? last : ntiles_all;
-  }
+  int ntiles, nfull;
+  query_block_tiles<CAUSAL, kBwdTile>(sq, q0, kBwdOwn, &ntiles, &nfull);
+  const int lim = key_limit<CAUSAL>(sq, myq);
+  const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
 
   u32x4 kreg[L::PER_THREAD], vreg[L::PER_THREAD];
   auto load_tile = [&](int j) {
@@ -315,7 +329,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       const int c = tid + i * kBwdThreads;
       const int row = c / L::CPR, cc = c - row * L::CPR;
       const int key = k0 + row;
-      if (key < N) {
+      if (key < sq.lk) {
         const size_t off = (size_t)key * D + cc * (16 / sizeof(T));
         kreg[i] = *reinterpret_cast<const u32x4*>(Kp + off);
         vreg[i] = *reinterpret_cast<const u32x4*>(Vp + off);
@@ -341,18 +355,22 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   for (int mb = 0; mb < MB; ++mb) dqacc[mb] = f32x16{};
   const float c = a.c;
 
-  load_tile(0);
-  store_tile(0);
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
     if (j + 1 < ntiles) load_tile(j + 1);
     const int k0 = j * kBwdTile;
-    if (!CAUSAL || k0 <= qw + 31) {
+    if (!CAUSAL || k0 <= wlast) {
       const T* kt = lds_k + buf * L::TILE;
       const T* vt = lds_v + buf * L::TILE;
-      const bool edge = (k0 + kBwdTile > N) || (CAUSAL && k0 + kBwdTile - 1 > qw);
+      // unmasked when every row of the wave may see every key of the tile
+      const bool edge = j >= nfull && ((k0 + kBwdTile > sq.lk) || (CAUSAL && k0 + kBwdTile - 1 > qw + sq.off) ||
+                                       qw + 31 >= sq.lq);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -369,8 +387,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
           float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
           if (edge) {
             const int key = k0 + 32 * kb + acc_row(r, h);
-            const bool ok = key < N && (!CAUSAL || key <= myq);
-            p = ok ? p : 0.0f;
+            p = key <= lim ? p : 0.0f;
           }
           dp[r] = p * (dp[r] - dq_d);
         }
@@ -388,16 +405,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (myq < N) {
-    T* dqrow = reinterpret_cast<T*>(a.dq) + head + (size_t)myq * D;
+  if (myq < Nq) {  // padding rows store zeros
+    T* dqrow = reinterpret_cast<T*>(a.dq) + headq + (size_t)myq * D;
+    const bool real = myq < sq.lq;
     const float sc = a.scale;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * h;
-        store4<T>(dqrow + d0, dqacc[mb][4 * g] * sc, dqacc[mb][4 * g + 1] * sc, dqacc[mb][4 * g + 2] * sc,
-                  dqacc[mb][4 * g + 3] * sc);
+        float q4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q4[u] = real ? dqacc[mb][4 * g + u] * sc : 0.0f;
+        store4<T>(dqrow + d0, q4[0], q4[1], q4[2], q4[3]);
       }
   }
 }
@@ -406,7 +426,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t stream) {
   if (stage == 0) {
-    const long long rows = (long long)p.B * p.H * p.N;
+    const long long rows = (long long)p.B * p.H * p.Nq;
     constexpr int LPR = D / (16 / sizeof(T));
     constexpr int RPB = 256 / LPR;
     const long long blocks = (rows + RPB - 1) / RPB;
@@ -417,10 +437,11 @@ static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t strea
   BwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.dout = p.dout; a.lse = p.lse;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.dvec = p.dvec;
-  a.N = p.N;
+  a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
-  a.nblk = (p.N + kBwdOwn - 1) / kBwdOwn;
+  a.nblk = ((stage == 1 ? p.Nk : p.Nq) + kBwdOwn - 1) / kBwdOwn;
   a.total = a.nblk * p.B * p.H;
   if (stage == 1)
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);

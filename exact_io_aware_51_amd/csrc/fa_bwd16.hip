@@ -29,7 +29,9 @@ struct Bwd16Args {
   void* dq;
   void* dk;
   void* dv;
-  int N;
+  const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
+  const int* seqlens_k;
+  int Nq, Nk, H;
   int nblk;
   int total;
   float c;      // scale * log2(e), signed
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
@@ -94,35 +96,33 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
   if (CAUSAL) qb = a.nblk - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
-  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + head;
-  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + head);
-  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + head);
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const size_t headq = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + headq;
+  const T* __restrict__ dO = reinterpret_cast<const T*>(a.dout) + headq;
+  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + headk);
+  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + headk);
 
   const int myq = qw + col;
   Frag qf[KSTEPS], dof[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
-    dof[ks] = myq < N ? row_frag<T>(dO + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
+    qf[ks] = myq < sq.lq ? row_frag<T>(Q + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
+    dof[ks] = myq < sq.lq ? row_frag<T>(dO + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
   }
-  const float lse2 = myq < N ? a.lse[(size_t)bh * N + myq] * kLog2e : 0.0f;
-  const float dd = myq < N ? a.dvec[(size_t)bh * N + myq] : 0.0f;
+  const float lse2 = myq < sq.lq ? a.lse[(size_t)bh * Nq + myq] * kLog2e : 0.0f;
+  const float dd = myq < sq.lq ? a.dvec[(size_t)bh * Nq + myq] : 0.0f;
 
-  const int nt_all = (N + 63) / 64;
-  int nt = nt_all;
-  if (CAUSAL) {
-    const int last = (q0 + 127) / 64 + 1;
-    nt = last < nt_all ? last : nt_all;
-  }
-  const int nt_full = CAUSAL ? q0 / 64 : N / 64;
-  const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
+  // key tiles this block visits, and how many leading ones no real row sees masked
+  int nt, nt_full;
+  query_block_tiles<CAUSAL, 64>(sq, q0, 128, &nt, &nt_full);
+  const int lim = key_limit<CAUSAL>(sq, myq);
+  const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
 
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D>(goff, wave, lane);
   auto dma = [&](const char* g, int row0, int region) {
-    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i) lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
   };
@@ -174,8 +174,8 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
       dma(Vg, 64 * (j + 1), VREG + (vs2 ^ 1) * TL::BYTES);
     }
     const int k0 = 64 * j;
-    const bool act = FULL || !CAUSAL || k0 <= qw + 31;
-    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= qw + 31));
+    const bool act = FULL || !CAUSAL || k0 <= wlast;
+    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= wlast));
     if (act) {
       const int t0 = lim - k0 - 4 * h;
       // the two 32-key halves one after the other keeps two accumulators live, not four
@@ -219,41 +219,46 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  dma(Kg, 0, KREG);
-  dma(Vg, 0, VREG);
-  // tile 0 owes no dQ product yet: generic step
-  step(0, 0, 0, std::false_type{});
-  int j = 1;
-  // mask-free steps, six at a time so that every LDS offset is a constant
-  for (; j + 5 < nt_full; j += 6) {
-    step(j, I1{}, I1{}, std::true_type{});
-    step(j + 1, I2{}, I0{}, std::true_type{});
-    step(j + 2, I0{}, I1{}, std::true_type{});
-    step(j + 3, I1{}, I0{}, std::true_type{});
-    step(j + 4, I2{}, I1{}, std::true_type{});
-    step(j + 5, I0{}, I0{}, std::true_type{});
+  if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
+    dma(Kg, 0, KREG);
+    dma(Vg, 0, VREG);
+    // tile 0 owes no dQ product yet: generic step
+    step(0, 0, 0, std::false_type{});
+    int j = 1;
+    // mask-free steps, six at a time so that every LDS offset is a constant
+    for (; j + 5 < nt_full; j += 6) {
+      step(j, I1{}, I1{}, std::true_type{});
+      step(j + 1, I2{}, I0{}, std::true_type{});
+      step(j + 2, I0{}, I1{}, std::true_type{});
+      step(j + 3, I1{}, I0{}, std::true_type{});
+      step(j + 4, I2{}, I1{}, std::true_type{});
+      step(j + 5, I0{}, I0{}, std::true_type{});
+    }
+    // the rest (up to five mask-free tiles, then the masked ones): runtime stages
+    for (; j < nt; ++j) {
+      if (j < nt_full)
+        step(j, j % 3, j & 1, std::true_type{});
+      else
+        step(j, j % 3, j & 1, std::false_type{});
+    }
+    wait_vmem();
+    __builtin_amdgcn_s_barrier();
+    if (!CAUSAL || 64 * (nt - 1) <= wlast) dq_prev((nt - 1) % 3);
   }
-  // the rest (up to five mask-free tiles, then the masked ones): runtime stages
-  for (; j < nt; ++j) {
-    if (j < nt_full)
-      step(j, j % 3, j & 1, std::true_type{});
-    else
-      step(j, j % 3, j & 1, std::false_type{});
-  }
-  wait_vmem();
-  __builtin_amdgcn_s_barrier();
-  if (!CAUSAL || 64 * (nt - 1) <= qw + 31) dq_prev((nt - 1) % 3);
 
-  if (myq < N) {
-    T* row = reinterpret_cast<T*>(a.dq) + head + (size_t)myq * D;
+  if (myq < Nq) {  // padding rows store zeros
+    T* row = reinterpret_cast<T*>(a.dq) + headq + (size_t)myq * D;
+    const bool real = myq < sq.lq;
     const float sc = a.scale;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * h;
-        store4<T>(row + d0, dqacc[mb][4 * g] * sc, dqacc[mb][4 * g + 1] * sc, dqacc[mb][4 * g + 2] * sc,
-                  dqacc[mb][4 * g + 3] * sc);
+        float q4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q4[u] = real ? dqacc[mb][4 * g + u] * sc : 0.0f;
+        store4<T>(row + d0, q4[0], q4[1], q4[2], q4[3]);
       }
   }
 }
@@ -285,44 +290,53 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
   const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   const int kb0 = kblk * 128;
   const int kw = kb0 + 32 * wave;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const char* Qg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + head);
-  const char* Og = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + head);
-  const float* lse = a.lse + (size_t)bh * N;
-  const float* dvec = a.dvec + (size_t)bh * N;
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const size_t headq = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
+  const char* Qg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + headq);
+  const char* Og = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + headq);
+  const float* lse = a.lse + (size_t)bh * Nq;
+  const float* dvec = a.dvec + (size_t)bh * Nq;
 
   const int mykey = kw + col;
   Frag kf[KSTEPS], vf[KSTEPS];
   {
-    const T* Kp = reinterpret_cast<const T*>(a.k) + head;
-    const T* Vp = reinterpret_cast<const T*>(a.v) + head;
+    const T* Kp = reinterpret_cast<const T*>(a.k) + headk;
+    const T* Vp = reinterpret_cast<const T*>(a.v) + headk;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      kf[ks] = mykey < N ? row_frag<T>(Kp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
-      vf[ks] = mykey < N ? row_frag<T>(Vp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
+      kf[ks] = mykey < sq.lk ? row_frag<T>(Kp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
+      vf[ks] = mykey < sq.lk ? row_frag<T>(Vp + (size_t)mykey * D + ks * 16, h) : zero_frag<T>();
     }
   }
 
-  const int nt = (N + 63) / 64;
-  const int first = CAUSAL ? kb0 / 64 : 0;
-  // query tiles every wave sees unmasked: [full0, full1)
-  const int full0 = CAUSAL ? (kb0 + 127) / 64 + 1 : 0;
-  const int full1 = N / 64;
+  // query tiles of real queries; under the causal mask key j is first seen by
+  // query j - off.  A block of padding keys visits none.
+  const int nt = kb0 < sq.lk ? (sq.lq + 63) / 64 : 0;
+  int first = 0, full0 = 0;
+  if (CAUSAL) {
+    const int f = floor_div(kb0 - sq.off, 64);
+    first = f > 0 ? f : 0;
+    // query tiles every wave sees unmasked: [full0, full1); the block's last
+    // key kb0 + 127 is seen by every query from kb0 + 127 - off on
+    const int g = floor_div(kb0 + 127 - sq.off + 63, 64);
+    full0 = g > first ? g : first;
+  }
+  const int full1 = sq.lq / 64;
 
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D>(goff, wave, lane);
   float lse_next = 0.0f, d_next = 0.0f;  // wave 0 stages the next tile's per-row values
   auto fetch = [&](int i, int stage) {
     const int row0 = 64 * i;
-    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
-    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lq - row0) * TL::ROWB);
+    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lq - row0) * TL::ROWB);
 #pragma unroll
     for (int r = 0; r < TL::ROUNDS; ++r) {
       lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * 4 + wave) * 1024, goff[r]);
@@ -330,8 +344,8 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
     }
     if (wave == 0) {
       const int qi = row0 + lane;
-      lse_next = qi < N ? -lse[qi] * kLog2e : 0.0f;
-      d_next = qi < N ? dvec[qi] : 0.0f;
+      lse_next = qi < sq.lq ? -lse[qi] * kLog2e : 0.0f;
+      d_next = qi < sq.lq ? dvec[qi] : 0.0f;
     }
   };
   auto publish = [&](int stage) {  // wave 0 writes the staged per-row values
@@ -366,7 +380,7 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
     __builtin_amdgcn_s_barrier();
     if (i + 1 < nt) fetch(i + 1, st ^ 1);
     const int i0 = 64 * i;
-    if (!FULL && CAUSAL && i0 + 63 < kw) return;  // every query of the tile precedes this wave's keys
+    if (!FULL && CAUSAL && i0 + 63 + sq.off < kw) return;  // no query of the tile sees this wave's keys
     const int qo = QREG + st * TL::BYTES, oo = OREG + st * TL::BYTES;
     const float* lt = reinterpret_cast<const float*>(smem + LREG) + st * 64;
     const float* dt = reinterpret_cast<const float*>(smem + DREG) + st * 64;
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
           float p = fast_exp2(__builtin_fmaf(s[r], c, l4[u]));
           if constexpr (!FULL) {
             const int qi = i0 + rr + u;
-            p = (qi < N && (!CAUSAL || mykey <= qi)) ? p : 0.0f;
+            p = (qi < sq.lq && (!CAUSAL || mykey <= qi + sq.off)) ? p : 0.0f;
           }
           s[r] = p;
           dp[r] = p * (dp[r] - d4[u]);
@@ -452,18 +466,24 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
     }
   }
 
-  if (mykey < N) {
-    T* dkrow = reinterpret_cast<T*>(a.dk) + head + (size_t)mykey * D;
-    T* dvrow = reinterpret_cast<T*>(a.dv) + head + (size_t)mykey * D;
+  if (mykey < Nk) {  // padding keys store zeros
+    T* dkrow = reinterpret_cast<T*>(a.dk) + headk + (size_t)mykey * D;
+    T* dvrow = reinterpret_cast<T*>(a.dv) + headk + (size_t)mykey * D;
+    const bool real = mykey < sq.lk;
     const float sc = a.scale;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * h;
-        store4<T>(dkrow + d0, dkacc[mb][4 * g] * sc, dkacc[mb][4 * g + 1] * sc, dkacc[mb][4 * g + 2] * sc,
-                  dkacc[mb][4 * g + 3] * sc);
-        store4<T>(dvrow + d0, dvacc[mb][4 * g], dvacc[mb][4 * g + 1], dvacc[mb][4 * g + 2], dvacc[mb][4 * g + 3]);
+        float k4[4], v4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          k4[u] = real ? dkacc[mb][4 * g + u] * sc : 0.0f;
+          v4[u] = real ? dvacc[mb][4 * g + u] : 0.0f;
+        }
+        store4<T>(dkrow + d0, k4[0], k4[1], k4[2], k4[3]);
+        store4<T>(dvrow + d0, v4[0], v4[1], v4[2], v4[3]);
       }
   }
 }
@@ -473,10 +493,11 @@ static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
   Bwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
-  a.N = p.N;
+  a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
-  a.nblk = (p.N + 127) / 128;
+  a.nblk = (p.Nk + 127) / 128;
   a.total = a.nblk * p.B * p.H;
   hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -497,10 +518,11 @@ static hipError_t launch_dq16_t(const BwdProblem& p, hipStream_t stream) {
   Bwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
-  a.N = p.N;
+  a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
-  a.nblk = (p.N + 127) / 128;
+  a.nblk = (p.Nq + 127) / 128;
   a.total = a.nblk * p.B * p.H;
   hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();

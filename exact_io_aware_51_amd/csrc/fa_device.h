@@ -201,6 +201,60 @@ __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t 
 // Wave-uniform "does any lane want this".
 __device__ inline bool any_lane(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
 
+// Floor of a / b for b > 0 and any sign of a.
+__device__ inline int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
+
+// Geometry of one sequence of a batch: lq real queries of Nq rows, lk real
+// keys of Nk rows (lengths from the optional device arrays, clamped into
+// [0, Nq] / [0, Nk]).  The queries are the last lq positions of the key
+// sequence, so under the causal mask query i may see key j iff j <= i + off,
+// off = lk - lq; with equal counts and no lengths this is j <= i.
+struct Seq {
+  int lq, lk, off;
+};
+
+__device__ inline Seq seq_of(const int* seqlens_q, const int* seqlens_k, int b, int Nq, int Nk) {
+  int lq = Nq, lk = Nk;
+  if (seqlens_q != nullptr) {
+    const int x = seqlens_q[b];
+    lq = x < 0 ? 0 : (x > Nq ? Nq : x);
+  }
+  if (seqlens_k != nullptr) {
+    const int x = seqlens_k[b];
+    lk = x < 0 ? 0 : (x > Nk ? Nk : x);
+  }
+  lq = __builtin_amdgcn_readfirstlane(lq);
+  lk = __builtin_amdgcn_readfirstlane(lk);
+  return {lq, lk, lk - lq};
+}
+
+// Largest key query row i may see; negative when it sees none (a padding row,
+// or a causal row that starts before the first key).
+template <bool CAUSAL>
+__device__ inline int key_limit(const Seq& s, int i) {
+  if (i >= s.lq) return -1;
+  const int lim = CAUSAL ? i + s.off : s.lk - 1;
+  return lim < s.lk - 1 ? lim : s.lk - 1;
+}
+
+// Key tiles of width BN that a block of query rows [q0, q0 + rows) visits
+// (*nt), and how many leading ones no real row of the block sees masked (*nfull).
+template <bool CAUSAL, int BN>
+__device__ inline void query_block_tiles(const Seq& s, int q0, int rows, int* nt, int* nfull) {
+  const int last = (q0 + rows - 1 < s.lq - 1 ? q0 + rows - 1 : s.lq - 1);  // last real row
+  if (last < q0) {
+    *nt = 0;
+    *nfull = 0;
+    return;
+  }
+  const int kmax = key_limit<CAUSAL>(s, last);
+  const int kmin = key_limit<CAUSAL>(s, q0);  // the limit only grows with the row
+  const int n = kmax < 0 ? 0 : kmax / BN + 1;
+  const int f = kmin < 0 ? 0 : (kmin + 1) / BN;
+  *nt = n;
+  *nfull = f < n ? f : n;
+}
+
 // Store 4 consecutive elements (fp32 in) as T.
 template <typename T>
 __device__ inline void store4(T* p, float a, float b, float c, float d) {

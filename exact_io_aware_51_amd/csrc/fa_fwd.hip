@@ -31,7 +31,9 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int N;
+  const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
+  const int* seqlens_k;
+  int Nq, Nk, H;
   int nqb;     // query blocks per head
   int total;   // workgroups in the grid
   float c;     // |scale| * log2(e)
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
 
   // block coordinates are wave-uniform; keep them (and every address built
   // from them) in scalar registers
@@ -110,31 +112,29 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   if (CAUSAL) qb = a.nqb - 1 - qb;  // the longest causal rows start first
   const int q0 = qb * kFwdBM;
   const int qw = q0 + wave * 32;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
-  const char* Kb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + head);
-  const char* Vb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + head);
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * (size_t)Nq * D;
+  const char* Kb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + (size_t)bh * (size_t)Nk * D);
+  const char* Vb = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + (size_t)bh * (size_t)Nk * D);
 
   // Q rows of this lane's query column, as B fragments (k = d).
   const int myq = qw + col;
   Frag qf[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
+    qf[ks] = myq < sq.lq ? row_frag<T>(Q + (size_t)myq * D + ks * M::KS, h) : zero_frag<T>();
     if (a.negate) qf[ks] = neg_frag<T>(qf[ks]);
   }
 
-  const int ntiles_all = (N + kFwdBN - 1) / kFwdBN;
-  int ntiles = ntiles_all;
-  if (CAUSAL) {
-    const int last = (q0 + kFwdBM - 1) / kFwdBN + 1;
-    ntiles = last < ntiles_all ? last : ntiles_all;
-  }
-  // largest key this lane's query may see
-  const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
+  int ntiles, nfull;
+  query_block_tiles<CAUSAL, kFwdBN>(sq, q0, kFwdBM, &ntiles, &nfull);
+  // largest key this lane's query may see (negative: none)
+  const int lim = key_limit<CAUSAL>(sq, myq);
+  const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
 
   // Global -> register staging of one K/V tile: 16-byte chunks, coalesced.
-  // The buffer view of the tile ends at key N, so reads past it return zeros.
+  // The buffer view of the tile ends at the sequence's last key, so reads
+  // past it return zeros.
   uint32_t goff[L::PER_THREAD], soff[L::PER_THREAD], voff[L::PER_THREAD];
 #pragma unroll
   for (int i = 0; i < L::PER_THREAD; ++i) {
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   u32x4 kreg[L::PER_THREAD], vreg[L::PER_THREAD];
   auto load_tile = [&](int j) {
     const uint32_t base = (uint32_t)(j * kFwdBN) * L::ROWB;
-    const uint32_t left = (uint32_t)(N - j * kFwdBN) * L::ROWB;
+    const uint32_t left = (uint32_t)(sq.lk - j * kFwdBN) * L::ROWB;
     const auto rk = buffer_rsrc(Kb + base, left);
     const auto rv = buffer_rsrc(Vb + base, left);
 #pragma unroll
@@ -250,8 +250,10 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
 #endif
   };
 
-  load_tile(0);
-  store_tile(0);
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
@@ -259,10 +261,12 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
     if (j + 1 < ntiles) load_tile(j + 1);
     const int k0 = j * kFwdBN;
     // waves whose rows all precede this tile's first key have nothing to do
-    if (!CAUSAL || k0 <= qw + 31) {
+    if (!CAUSAL || k0 <= wlast) {
       const T* kt = lds_k + buf * L::KTILE;
       const T* vt = lds_v + buf * L::VTILE;
-      const bool edge = (k0 + kFwdBN > N) || (CAUSAL && k0 + kFwdBN - 1 > qw);
+      // a tile is unmasked for the wave when every row of it may see every key
+      const bool edge = j >= nfull && ((k0 + kFwdBN > sq.lk) || (CAUSAL && k0 + kFwdBN - 1 > qw + sq.off) ||
+                                       qw + 31 >= sq.lq);
       if (edge)
         tile(kt, vt, k0, std::true_type{});
       else
@@ -272,21 +276,25 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
     __syncthreads();
   }
 
-  // Epilogue: O = O_acc / l, LSE = ln(2^m * l).
+  // Epilogue: O = O_acc / l, LSE = ln(2^m * l); padding rows and rows that
+  // see no key store O = 0, LSE = -inf.
   l = halves_sum(l);
-  if (myq < N) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    T* orow = reinterpret_cast<T*>(a.o) + head + (size_t)myq * D;
+  if (myq < Nq) {
+    const bool real = myq < sq.lq && l > 0.0f;
+    const float inv = real ? 1.0f / l : 0.0f;
+    T* orow = reinterpret_cast<T*>(a.o) + (size_t)bh * (size_t)Nq * D + (size_t)myq * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * h;
-        store4<T>(orow + d0, oacc[mb][4 * g] * inv, oacc[mb][4 * g + 1] * inv,
-                  oacc[mb][4 * g + 2] * inv, oacc[mb][4 * g + 3] * inv);
+        float o4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o4[u] = real ? oacc[mb][4 * g + u] * inv : 0.0f;
+        store4<T>(orow + d0, o4[0], o4[1], o4[2], o4[3]);
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[(size_t)bh * N + myq] = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+      a.lse[(size_t)bh * Nq + myq] = real ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
   }
 }
 
@@ -294,8 +302,9 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   FwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
-  a.N = p.N;
-  a.nqb = (p.N + kFwdBM - 1) / kFwdBM;
+  a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
+  a.nqb = (p.Nq + kFwdBM - 1) / kFwdBM;
   a.total = a.nqb * p.B * p.H;
   const float sc = p.scale;
   a.negate = sc < 0.0f;

@@ -41,7 +41,9 @@ struct Fwd16Args {
   const void* v;
   void* o;
   float* lse;
-  int N;
+  const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
+  const int* seqlens_k;
+  int Nq, Nk, H;
   int nqb;
   int total;
   float c;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
-  const int N = a.N;
+  const int Nq = a.Nq, Nk = a.Nk;
 
   const int bid = xcd_remap(blockIdx.x, a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
@@ -88,34 +90,30 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + head;
-  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + head);
-  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + head);
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q) + (size_t)bh * (size_t)Nq * D;
+  const char* Kg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.k) + (size_t)bh * (size_t)Nk * D);
+  const char* Vg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.v) + (size_t)bh * (size_t)Nk * D);
 
   const int myq = qw + col;
   Frag qf[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
-    qf[ks] = myq < N ? row_frag<T>(Q + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
+    qf[ks] = myq < sq.lq ? row_frag<T>(Q + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
     if (a.negate) qf[ks] = neg_frag<T>(qf[ks]);
   }
 
-  const int nt_all = (N + BN - 1) / BN;
-  int nt = nt_all;  // key tiles this block visits
-  if (CAUSAL) {
-    const int last = (q0 + 127) / BN + 1;
-    nt = last < nt_all ? last : nt_all;
-  }
-  // tiles every wave of the block sees unmasked
-  const int nt_full = CAUSAL ? q0 / BN : N / BN;
-  const int lim = CAUSAL ? (myq < N - 1 ? myq : N - 1) : N - 1;
+  // key tiles this block visits, and how many leading ones no real row sees masked
+  int nt, nt_full;
+  query_block_tiles<CAUSAL, BN>(sq, q0, 128, &nt, &nt_full);
+  const int lim = key_limit<CAUSAL>(sq, myq);
+  const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
 
   // ---- direct loads: lane's source offset inside a tile, per round
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D, BN>(goff, wave, lane);
   auto dma = [&](const char* g, int row0, int region) {
-    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(N - row0) * TL::ROWB);
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i)
       lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
@@ -169,8 +167,8 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     dma(Vg, BN * j, VREG + KST * TL::BYTES);
 
     const int k0 = BN * j;
-    const bool act = FULL || !CAUSAL || k0 <= qw + 31;
-    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - BN <= qw + 31));
+    const bool act = FULL || !CAUSAL || k0 <= wlast;
+    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - BN <= wlast));
     if (act) {
 #if FA16_PRIO
       __builtin_amdgcn_s_setprio(1);
@@ -300,47 +298,53 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     }
   };
 
-  dma(Kg, 0, KREG);
-  step(0, std::integral_constant<int, 0>{}, std::false_type{});
-  int j = 1;
-  for (; j + 1 < nt_full; j += 2) {
-    step(j, std::integral_constant<int, 1>{}, std::true_type{});
-    step(j + 1, std::integral_constant<int, 0>{}, std::true_type{});
-  }
-  if (j < nt_full) {
-    step(j, std::integral_constant<int, 1>{}, std::true_type{});
-    ++j;
-  }
-  for (; j < nt; ++j) {
-    if (j & 1)
-      step(j, std::integral_constant<int, 1>{}, std::false_type{});
-    else
-      step(j, std::integral_constant<int, 0>{}, std::false_type{});
-  }
-  // the last tile's P still owes its V product
-  wait_vmem();
-  __builtin_amdgcn_s_barrier();
-  if (!CAUSAL || BN * (nt - 1) <= qw + 31) {
-    if ((nt - 1) & 1)
-      pv(1);
-    else
-      pv(0);
+  if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
+    dma(Kg, 0, KREG);
+    step(0, std::integral_constant<int, 0>{}, std::false_type{});
+    int j = 1;
+    for (; j + 1 < nt_full; j += 2) {
+      step(j, std::integral_constant<int, 1>{}, std::true_type{});
+      step(j + 1, std::integral_constant<int, 0>{}, std::true_type{});
+    }
+    if (j < nt_full) {
+      step(j, std::integral_constant<int, 1>{}, std::true_type{});
+      ++j;
+    }
+    for (; j < nt; ++j) {
+      if (j & 1)
+        step(j, std::integral_constant<int, 1>{}, std::false_type{});
+      else
+        step(j, std::integral_constant<int, 0>{}, std::false_type{});
+    }
+    // the last tile's P still owes its V product
+    wait_vmem();
+    __builtin_amdgcn_s_barrier();
+    if (!CAUSAL || BN * (nt - 1) <= wlast) {
+      if ((nt - 1) & 1)
+        pv(1);
+      else
+        pv(0);
+    }
   }
 
+  // padding rows and rows that see no key store O = 0, LSE = -inf
   l = halves_sum(l);
-  if (myq < N) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    T* orow = reinterpret_cast<T*>(a.o) + head + (size_t)myq * D;
+  if (myq < Nq) {
+    const bool real = myq < sq.lq && l > 0.0f;
+    const float inv = real ? 1.0f / l : 0.0f;
+    T* orow = reinterpret_cast<T*>(a.o) + (size_t)bh * (size_t)Nq * D + (size_t)myq * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * mb + 8 * g + 4 * h;
-        store4<T>(orow + d0, oacc[mb][4 * g] * inv, oacc[mb][4 * g + 1] * inv, oacc[mb][4 * g + 2] * inv,
-                  oacc[mb][4 * g + 3] * inv);
+        float o4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o4[u] = real ? oacc[mb][4 * g + u] * inv : 0.0f;
+        store4<T>(orow + d0, o4[0], o4[1], o4[2], o4[3]);
       }
     if (a.lse != nullptr && h == 0)
-      a.lse[(size_t)bh * N + myq] = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+      a.lse[(size_t)bh * Nq + myq] = real ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
   }
 }
 
@@ -348,8 +352,9 @@ template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   Fwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
-  a.N = p.N;
-  a.nqb = (p.N + 127) / 128;
+  a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
+  a.nqb = (p.Nq + 127) / 128;
   a.total = a.nqb * p.B * p.H;
   const float sc = p.scale;
   a.negate = sc < 0.0f;

@@ -6,13 +6,17 @@
 
 namespace fa {
 
+// q, o: [B, H, Nq, d]; k, v: [B, H, Nk, d]; lse: [B, H, Nq].  seqlens_q /
+// seqlens_k: optional device int32[B] sequence lengths (nullptr: Nq / Nk).
 struct FwdProblem {
   const void* q;
   const void* k;
   const void* v;
   void* o;
   float* lse;
-  int B, H, N, d;
+  int B, H, Nq, Nk, d;
+  const int* seqlens_q;
+  const int* seqlens_k;
   float scale;
   int causal;
   int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
@@ -28,8 +32,10 @@ struct BwdProblem {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;  // workspace: fp32 [B*H*N] row sums D_i
-  int B, H, N, d;
+  float* dvec;  // workspace: fp32 [B*H*Nq] row sums D_i
+  int B, H, Nq, Nk, d;
+  const int* seqlens_q;
+  const int* seqlens_k;
   float scale;
   int causal;
   int dtype;

@@ -92,3 +92,17 @@ def shape_case(B, H, N, d, dtype, causal, seed, mode="fwd+bwd", q_scale=1.0):
     """A non-standard shape for parity sweeps, drawn with the same recipe."""
     return Workload(f"B{B}H{H}N{N}d{d}{dtype}{'c' if causal else ''}", mode, dtype,
                     B, H, N, d, causal, q_scale=q_scale, seed=seed)
+
+
+def kv_inputs(B, H, Nq, Nk, d, dtype, seed, with_grad=True):
+    """q [B,H,Nq,d], k and v [B,H,Nk,d] (and do [B,H,Nq,d]): N(0,1) fp32 draws cast to `dtype`."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, Nk, d), generator=g, dtype=torch.float32)
+    out = [q, k, v]
+    if with_grad:
+        out.append(torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32))
+    dt = DTYPES[dtype]
+    return tuple(x.to(dt) for x in out)

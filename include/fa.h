@@ -119,6 +119,46 @@ int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, con
               const void *workspace, size_t workspace_bytes, void *dq,
               int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
 
+/*
+ * Unequal query and key counts, and padded batches.  The pages apply causal
+ * masking "for autoregressive decoding" and apply causal masking and padding
+ * per tile ("How Flash Attention Works", sections "How Flash Attention Works:
+ * The Exact-Attention Idea" and "Tiling Q, K, and V for Fast On-Chip
+ * Memory"); they fix neither the causal alignment for unequal counts nor the
+ * output of padding rows, and these entry points take the readings below.
+ *   q, o, dout, dq : [B,H,Nq,d];  k, v, dk, dv : [B,H,Nk,d];  lse : fp32 [B,H,Nq]
+ *   seqlens_q, seqlens_k : NULL, or device pointers to int32[B] (4-byte
+ *       aligned): sequence b has lq_b = seqlens_q[b] real queries and
+ *       lk_b = seqlens_k[b] real keys; NULL means Nq (Nk) for every b.
+ *       Values are read on the device and clamped into [0, Nq] / [0, Nk],
+ *       so an out-of-range length cannot make a kernel read or write outside
+ *       the arrays.  They must stay unchanged until the queued work is done.
+ *   Causal mask, bottom-right aligned: the lq_b queries are the last lq_b
+ *       positions of the lk_b-key sequence, so query i sees key j iff
+ *       j <= i + (lk_b - lq_b).  With Nq = Nk and no lengths this is fa_fwd /
+ *       fa_bwd exactly; with one query (decoding against a key cache) the
+ *       query sees every key.
+ *   Rows past a length (padding), and rows that see no key (causal with
+ *       lq_b > lk_b, or lk_b = 0), get o = 0 and lse = -inf; they contribute
+ *       nothing to any gradient, and dq rows past lq_b and dk / dv rows past
+ *       lk_b are written as 0.
+ * Other conventions, validation and errors are those of fa_fwd / fa_bwd, with
+ * Nq >= 1, Nk >= 1, B*H*Nq < 2^31 and B*H*Nk < 2^31.  fa_bwd_kv's workspace is
+ * fa_bwd_workspace_bytes(B, H, Nq, d, dtype); its o and lse must come from
+ * fa_fwd_kv with the same arguments.
+ */
+int fa_fwd_kv(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int Nq, int Nk, int d,
+              const int *seqlens_q, const int *seqlens_k,
+              float scale, int causal, fa_dtype dtype, void *stream);
+int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o,
+              const void *dout, const float *lse,
+              void *dq, void *dk, void *dv,
+              void *workspace, size_t workspace_bytes,
+              int B, int H, int Nq, int Nk, int d,
+              const int *seqlens_q, const int *seqlens_k,
+              float scale, int causal, fa_dtype dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -38,7 +38,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv",
-                                  "fa_bwd_dq", "fa_status_string", "fa_version"])
+                                  "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -145,12 +145,67 @@ def test_bwd_stages_reject(fa, name, call, want):
     assert call(fa) == want
 
 
+# Unequal counts: q/o hold Nq = 256 rows, k/v Nk = 1024 rows per (b, h); with
+# B = 1, H = 2, d = 64, bf16 that is 65536 B for q and 262144 B for k.
+KV_K_BYTES = 2 * 1024 * 64 * 2
+
+
+def _fwd_kv(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, Nq=256, Nk=1024, d=64,
+             sq=_ptr(10), sk=_ptr(11), scale=0.125, causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_kv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                        a["sq"], a["sk"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def _bwd_kv(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), dout=_ptr(4), lse=_ptr(5), dq=_ptr(6),
+             dk=_ptr(7), dv=_ptr(8), ws=_ptr(9), wsb=1 << 20, B=1, H=2, Nq=256, Nk=1024, d=64,
+             sq=_ptr(10), sk=_ptr(11), scale=0.125, causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_kv(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                        a["ws"], a["wsb"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["sq"], a["sk"],
+                        a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+KV_FWD_BAD = [
+    ("Nq=0", dict(Nq=0), -1), ("Nk=0", dict(Nk=0), -1), ("Nk<0", dict(Nk=-5), -1),
+    ("huge B*H*Nk", dict(B=1 << 16, H=1 << 10, Nk=1 << 10), -1),
+    ("misaligned seqlens_q", dict(sq=_ptr(10, 2)), -1), ("misaligned seqlens_k", dict(sk=_ptr(11, 1)), -1),
+    ("d=48", dict(d=48), -2), ("causal 3", dict(causal=3), -1), ("null v", dict(v=None), -1),
+    ("o inside k (sized by Nk)", dict(o=_ptr(1, KV_K_BYTES - 4096)), -1),
+    ("o over seqlens_q", dict(o=_ptr(10)), -1), ("lse over seqlens_k", dict(lse=_ptr(11)), -1),
+]
+
+KV_BWD_BAD = [
+    ("Nk=0", dict(Nk=0), -1), ("misaligned seqlens_k", dict(sk=_ptr(11, 2)), -1),
+    ("workspace sized by Nq", dict(wsb=2 * 256 * 4 - 4), -3),
+    ("dk inside v (sized by Nk)", dict(dk=_ptr(2, KV_K_BYTES - 4096)), -1),
+    ("dq over seqlens_q", dict(dq=_ptr(10)), -1), ("dv over seqlens_k", dict(dv=_ptr(11)), -1),
+    ("workspace over seqlens_k", dict(ws=_ptr(11)), -3),
+    ("null dout", dict(dout=None), -1), ("dtype 9", dict(dtype=9), -2),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", KV_FWD_BAD, ids=[x[0] for x in KV_FWD_BAD])
+def test_fwd_kv_rejects(fa, name, kw, want):
+    assert _fwd_kv(fa, **kw) == want
+
+
+@pytest.mark.parametrize("name,kw,want", KV_BWD_BAD, ids=[x[0] for x in KV_BWD_BAD])
+def test_bwd_kv_rejects(fa, name, kw, want):
+    assert _bwd_kv(fa, **kw) == want
+
+
 @pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
 def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd(fa) == fa.FA_ERR_HIP
     assert _fwd(fa, lse=None, causal=1, dtype=fa.FA_F32, scale=-1.0) == fa.FA_ERR_HIP
     assert _bwd(fa) == fa.FA_ERR_HIP
     assert fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(9), 1 << 20, 1, 2, 256, 64, fa.FA_BF16, None) == fa.FA_ERR_HIP
+    assert _fwd_kv(fa) == fa.FA_ERR_HIP
+    assert _fwd_kv(fa, sq=None, sk=None, Nq=1) == fa.FA_ERR_HIP
+    assert _bwd_kv(fa) == fa.FA_ERR_HIP
 
 
 def test_python_helpers_refuse_cpu_tensors(fa):
@@ -160,4 +215,8 @@ def test_python_helpers_refuse_cpu_tensors(fa):
         fa.forward(q, q, q)
     with pytest.raises(ValueError):
         fa.backward(q, q, q, q, torch.zeros(1, 1, 4), q)
+    with pytest.raises(ValueError):
+        fa.forward_kv(q, q, q, seqlens_q=[4])
+    with pytest.raises(ValueError):
+        fa.backward_kv(q, q, q, q, torch.zeros(1, 1, 4), q)
     assert math.isclose(1 / math.sqrt(64), 0.125)

@@ -1,0 +1,155 @@
+"""GPU parity for unequal query/key counts and padded batches (fa_fwd_kv, fa_bwd_kv).
+
+The HIP path is compared with oracle.attention_forward_kv / attention_backward_kv
+on the same seeded inputs.  Readings under test (the pages fix neither): the
+queries are the last positions of their key sequence, so causal query i sees
+key j iff j <= i + lk - lq; padding rows and rows that see no key output O = 0
+and LSE = -inf, and the gradients of padding rows and keys are 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_51_amd as fa
+import oracle
+from exact_io_aware_51_amd import workloads as W
+from gates import GRAD_REL, check, check_lse, to_np
+from gpu_util import announce, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+
+# (B, H, Nq, Nk, d, seqlens_q, seqlens_k)
+CASES = [
+    (1, 2, 100, 300, 64, None, None),
+    (1, 2, 300, 100, 128, None, None),               # causal: the first 200 rows see no key
+    (2, 2, 1, 1000, 128, None, None),                # one query against a key cache
+    (1, 1, 129, 1, 64, None, None),
+    (3, 2, 257, 511, 64, [257, 100, 0], [511, 37, 200]),
+    (2, 2, 200, 200, 128, [200, 133], [65, 200]),
+    (2, 1, 512, 512, 128, [512, 384], [512, 448]),   # several full tiles with ragged ends
+]
+IDS = [f"B{c[0]}H{c[1]}q{c[2]}k{c[3]}d{c[4]}{'-ragged' if c[5] else ''}" for c in CASES]
+
+
+def _lens(x, dev):
+    return None if x is None else torch.tensor(x, dtype=torch.int32, device=dev)
+
+
+def _check_fwd(o, lse, ro, rl, dtype, what):
+    rl = np.asarray(rl)
+    empty = np.isinf(rl)
+    lse_np = to_np(lse)
+    assert np.array_equal(np.isinf(lse_np) & (lse_np < 0), empty), f"{what}: rows with LSE = -inf differ"
+    o_np = to_np(o)
+    assert np.all(o_np[empty] == 0.0), f"{what}: padding / empty rows are not exactly 0"
+    check(o, ro, dtype, f"{what} O")
+    if (~empty).any():
+        check_lse(lse_np[~empty], rl[~empty], dtype, f"{what} LSE")
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_fwd_kv_matches_oracle(dtype, causal, case):
+    dev = device()
+    B, H, Nq, Nk, d, lq, lk = case
+    seed = 7000 + 17 * Nq + Nk + d
+    announce("fwd_kv", dtype, causal, case, seed)
+    q, k, v = W.kv_inputs(B, H, Nq, Nk, d, dtype, seed, with_grad=False)
+    scale = 1.0 / float(np.sqrt(d))
+    o, lse = fa.forward_kv(*to_dev((q, k, v), dev), seqlens_q=_lens(lq, dev), seqlens_k=_lens(lk, dev),
+                           scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_kv(q, k, v, scale, causal, lq, lk)
+    _check_fwd(o, lse, ro, rl, dtype, f"fwd_kv {dtype} causal={causal} {case}")
+
+
+BWD_CASES = [CASES[0], CASES[1], CASES[2], CASES[4], CASES[5], CASES[6]]
+BWD_IDS = [IDS[CASES.index(c)] for c in BWD_CASES]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=BWD_IDS)
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_bwd_kv_matches_oracle(dtype, causal, case):
+    dev = device()
+    B, H, Nq, Nk, d, lq, lk = case
+    seed = 8000 + 17 * Nq + Nk + d
+    announce("bwd_kv", dtype, causal, case, seed)
+    q, k, v, do = W.kv_inputs(B, H, Nq, Nk, d, dtype, seed)
+    scale = 1.0 / float(np.sqrt(d))
+    qd, kd, vd, dod = to_dev((q, k, v, do), dev)
+    sq, sk = _lens(lq, dev), _lens(lk, dev)
+    o, lse = fa.forward_kv(qd, kd, vd, seqlens_q=sq, seqlens_k=sk, scale=scale, causal=causal)
+    dq, dk, dv = fa.backward_kv(qd, kd, vd, o, lse, dod, seqlens_q=sq, seqlens_k=sk, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attention_backward_kv(q, k, v, do, scale, causal, lq, lk)
+    tag = f"bwd_kv {dtype} causal={causal} {case}"
+    gate = GRAD_REL[dtype]
+    check(dq, rdq, dtype, f"{tag} dQ", rel_gate=gate)
+    check(dk, rdk, dtype, f"{tag} dK", rel_gate=gate)
+    check(dv, rdv, dtype, f"{tag} dV", rel_gate=gate)
+    # padding rows and keys are exactly zero
+    for b in range(B):
+        a = Nq if lq is None else lq[b]
+        c = Nk if lk is None else lk[b]
+        assert torch.all(dq[b, :, a:] == 0) and torch.all(dk[b, :, c:] == 0) and torch.all(dv[b, :, c:] == 0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_kv_equal_counts_is_the_square_path(dtype):
+    """Nq = Nk without lengths runs the same kernels as fa_fwd / fa_bwd: bit-identical."""
+    dev = device()
+    announce("kv equal counts", dtype)
+    q, k, v, do = to_dev(W.kv_inputs(2, 2, 333, 333, 128, dtype, 9001), dev)
+    for causal in (False, True):
+        o1, l1 = fa.forward(q, k, v, causal=causal)
+        o2, l2 = fa.forward_kv(q, k, v, causal=causal)
+        g1 = fa.backward(q, k, v, o1, l1, do, causal=causal)
+        g2 = fa.backward_kv(q, k, v, o2, l2, do, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
+
+
+def test_kv_lengths_are_clamped():
+    dev = device()
+    announce("kv clamped lengths")
+    q, k, v = to_dev(W.kv_inputs(2, 2, 130, 70, 64, "bf16", 9002, with_grad=False), dev)
+    a = fa.forward_kv(q, k, v, seqlens_q=[999, -5], seqlens_k=[70, 1 << 30], causal=True)
+    b = fa.forward_kv(q, k, v, seqlens_q=[130, 0], seqlens_k=[70, 70], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_decode_long_cache():
+    """One query per sequence against 32768 cached keys (bf16, d = 128), every head checked."""
+    dev = device()
+    announce("decode Nq=1 Nk=32768")
+    q, k, v = W.kv_inputs(2, 8, 1, 32768, 128, "bf16", 9003, with_grad=False)
+    lk = [32768, 20001]
+    o, lse = fa.forward_kv(*to_dev((q, k, v), dev), seqlens_k=_lens(lk, dev), scale=0.08838835, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_kv(q, k, v, 0.08838835, True, None, lk)
+    _check_fwd(o, lse, ro, rl, "bf16", "decode")
+
+
+def test_padded_batch_2048():
+    """A padded batch of four sequences at N = 2048 (bf16, d = 128, causal), forward and backward."""
+    dev = device()
+    announce("padded batch N=2048")
+    lq, lk = [2048, 1500, 777, 1], [2048, 1500, 777, 1]
+    q, k, v, do = W.kv_inputs(4, 2, 2048, 2048, 128, "bf16", 9004)
+    qd, kd, vd, dod = to_dev((q, k, v, do), dev)
+    sq, sk = _lens(lq, dev), _lens(lk, dev)
+    o, lse = fa.forward_kv(qd, kd, vd, seqlens_q=sq, seqlens_k=sk, scale=0.08838835, causal=True)
+    dq, dk, dv = fa.backward_kv(qd, kd, vd, o, lse, dod, seqlens_q=sq, seqlens_k=sk, scale=0.08838835, causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward_kv(q, k, v, 0.08838835, True, lq, lk)
+    _check_fwd(o, lse, ro, rl, "bf16", "padded 2048")
+    rdq, rdk, rdv = oracle.attention_backward_kv(q, k, v, do, 0.08838835, True, lq, lk)
+    for x, r, n in ((dq, rdq, "dQ"), (dk, rdk, "dK"), (dv, rdv, "dV")):
+        check(x, r, "bf16", f"padded 2048 {n}", rel_gate=GRAD_REL["bf16"])
