@@ -255,3 +255,55 @@ def attention_backward_kv(q, k, v, do, scale, causal, seqlens_q=None, seqlens_k=
             dq[b, h, :a] = scale * (ds @ kh)
             dk[b, h, :c] = scale * (ds.T @ qh)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse attention.  The pages name a block-sparse extension studied
+# alongside the dense algorithm as a separate configuration ("FlashAttention"
+# glossary entry, its definition) without fixing a mask format; the reading
+# taken here: a 0/1 mask
+# of shape [B, H, ceil(N / block), ceil(N / block)] removes every score of a
+# (query block, key block) pair whose entry is 0, on top of the causal mask.
+# Rows that see no key output O = 0 and LSE = -inf, as above.
+# ---------------------------------------------------------------------------
+
+
+def _block_visible(mask_bh, n, block):
+    """Elementwise n x n visibility from one head's block mask."""
+    idx = np.arange(n) // block
+    return np.asarray(mask_bh, dtype=bool)[idx[:, None], idx[None, :]]
+
+
+def attention_forward_sparse(q, k, v, scale, causal, block_mask, block=128):
+    """O and LSE for [B,H,N,d] inputs with a block mask [B, H, nb, nb] (nonzero = keep)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, _ = q.shape
+    bm = np.asarray(block_mask)
+    o = np.zeros(q.shape[:3] + (v.shape[3],))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            s = _scores_kv(q[b, h], k[b, h], scale, causal, 0)
+            s = np.where(_block_visible(bm[b, h], N, block), s, -np.inf)
+            p, lse[b, h] = _softmax_rows_kv(s)
+            o[b, h] = p @ v[b, h]
+    return o, lse
+
+
+def attention_backward_sparse(q, k, v, do, scale, causal, block_mask, block=128):
+    """dQ, dK, dV of L = sum(dO * O) for the block-sparse forward above."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, _ = q.shape
+    bm = np.asarray(block_mask)
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            s = _scores_kv(q[b, h], k[b, h], scale, causal, 0)
+            s = np.where(_block_visible(bm[b, h], N, block), s, -np.inf)
+            p, _ = _softmax_rows_kv(s)
+            dv[b, h] = p.T @ do[b, h]
+            dpm = do[b, h] @ v[b, h].T
+            dsm = p * (dpm - np.sum(p * dpm, axis=1, keepdims=True))
+            dq[b, h] = scale * (dsm @ k[b, h])
+            dk[b, h] = scale * (dsm.T @ q[b, h])
+    return dq, dk, dv

@@ -477,9 +477,130 @@ def pin_kv_finite_differences(orc):
             assert err < 1e-7, f"kv finite differences grad {which} causal={causal}: {err:.2e}"
 
 
+# ------------------------------------------------------------- block sparse
+# Reading (the pages name the extension, not a format): a 0/1 mask over
+# (query block, key block) pairs removes those scores, on top of the causal
+# mask; rows that see no key output O = 0 and LSE = -inf.
+def _mask_rand(seed, B, H, nb, p_keep=0.6):
+    m = (_rng(seed).random((B, H, nb, nb)) < p_keep).astype(np.uint8)
+    return m
+
+
+def pin_sparse_all_ones_is_dense(orc):
+    q, k, v = _qkv(50, 2, 2, 21, 8)
+    do = _rng(51).standard_normal(q.shape)
+    ones = np.ones((2, 2, 6, 6), dtype=np.uint8)
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.3, causal)
+        o2, lse2 = orc.attention_forward_sparse(q, k, v, 0.3, causal, ones, block=4)
+        _close(o2, o, 1e-13, f"sparse all-ones O causal={causal}")
+        _close(lse2, lse, 1e-13, f"sparse all-ones LSE causal={causal}")
+        for a, b, n in zip(orc.attention_backward_sparse(q, k, v, do, 0.3, causal, ones, block=4),
+                           orc.attention_backward(q, k, v, do, 0.3, causal), "QKV"):
+            _close(a, b, 1e-12, f"sparse all-ones d{n} causal={causal}")
+
+
+def pin_sparse_bruteforce(orc):
+    q, k, v = _qkv(52, 2, 2, 11, 3)
+    m = _mask_rand(53, 2, 2, 3)
+    m[0, 0, 1, :] = 0  # a query block that sees nothing
+    for causal in (False, True):
+        o, lse = orc.attention_forward_sparse(q, k, v, 0.6, causal, m, block=4)
+        for b in range(2):
+            for h in range(2):
+                n = 11
+                qq, kk, vv = q[b, h].tolist(), k[b, h].tolist(), v[b, h].tolist()
+                for i in range(n):
+                    js = [j for j in range(n) if m[b, h, i // 4, j // 4] and (not causal or j <= i)]
+                    if not js:
+                        assert np.all(o[b, h, i] == 0) and lse[b, h, i] == -math.inf, "sparse empty row"
+                        continue
+                    s = {j: 0.6 * math.fsum(x * y for x, y in zip(qq[i], kk[j])) for j in js}
+                    mx = max(s.values())
+                    w = {j: math.exp(s[j] - mx) for j in js}
+                    z = math.fsum(w.values())
+                    _close(lse[b, h, i], mx + math.log(z), 1e-12, f"sparse brute LSE b={b} h={h} i={i}")
+                    for c in range(3):
+                        _close(o[b, h, i, c], math.fsum(w[j] * vv[j][c] for j in js) / z, 1e-12,
+                               f"sparse brute O b={b} h={h} i={i}")
+
+
+def pin_sparse_block_diagonal(orc):
+    """A block-diagonal mask is attention inside each block, computed independently."""
+    q, k, v = _qkv(54, 1, 2, 14, 4)
+    do = _rng(55).standard_normal(q.shape)
+    eye = np.broadcast_to(np.eye(4, dtype=np.uint8), (1, 2, 4, 4)).copy()
+    for causal in (False, True):
+        o, lse = orc.attention_forward_sparse(q, k, v, 0.5, causal, eye, block=4)
+        g = orc.attention_backward_sparse(q, k, v, do, 0.5, causal, eye, block=4)
+        for c0 in range(0, 14, 4):
+            c1 = min(14, c0 + 4)
+            sl = (slice(None), slice(None), slice(c0, c1))
+            oc, lc = orc.attention_forward(q[sl], k[sl], v[sl], 0.5, causal)
+            _close(o[sl], oc, 1e-13, f"block-diagonal O chunk {c0} causal={causal}")
+            _close(lse[sl], lc, 1e-13, f"block-diagonal LSE chunk {c0}")
+            gc = orc.attention_backward(q[sl], k[sl], v[sl], do[sl], 0.5, causal)
+            for a, b, n in zip(g, gc, "QKV"):
+                _close(a[sl], b, 1e-12, f"block-diagonal d{n} chunk {c0} causal={causal}")
+
+
+def pin_sparse_torch_autograd(orc):
+    import torch
+    q, k, v = _qkv(56, 2, 2, 13, 5)
+    do = _rng(57).standard_normal(q.shape)
+    m = _mask_rand(58, 2, 2, 4)
+    m[1, 1, 2, :] = 0
+    vis = np.zeros((2, 2, 13, 13), dtype=bool)
+    idx = np.arange(13) // 4
+    for b in range(2):
+        for h in range(2):
+            vis[b, h] = m[b, h][idx[:, None], idx[None, :]].astype(bool)
+    for causal in (False, True):
+        allowed = vis & (np.tril(np.ones((13, 13), dtype=bool)) if causal else True)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        s = 0.4 * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+        s = s.masked_fill(~torch.tensor(allowed), float("-inf"))
+        rows = torch.tensor(allowed.any(axis=-1))
+        p = torch.where(rows[..., None], torch.softmax(torch.where(rows[..., None], s, torch.zeros_like(s)), dim=-1)
+                        * torch.tensor(allowed), torch.zeros_like(s))
+        p = p / torch.where(rows[..., None], p.sum(-1, keepdim=True), torch.ones_like(p[..., :1]))
+        out = torch.matmul(p, tv)
+        (out * torch.tensor(do)).sum().backward()
+        o, lse = orc.attention_forward_sparse(q, k, v, 0.4, causal, m, block=4)
+        _close(o, out.detach().numpy(), 1e-12, f"sparse autograd O causal={causal}")
+        dq, dk, dv = orc.attention_backward_sparse(q, k, v, do, 0.4, causal, m, block=4)
+        _close(dq, tq.grad.numpy(), 1e-10, f"sparse autograd dQ causal={causal}")
+        _close(dk, tk.grad.numpy(), 1e-10, f"sparse autograd dK causal={causal}")
+        _close(dv, tv.grad.numpy(), 1e-10, f"sparse autograd dV causal={causal}")
+
+
+def pin_sparse_finite_differences(orc):
+    q, k, v = _qkv(59, 1, 1, 7, 3)
+    do = _rng(60).standard_normal(q.shape)
+    m = np.array([[[[1, 0], [1, 1]]]], dtype=np.uint8)
+    for causal in (False, True):
+        grads = orc.attention_backward_sparse(q, k, v, do, 0.45, causal, m, block=4)
+        base = [q, k, v]
+        h = 1e-6
+        for which in range(3):
+            num = np.zeros_like(base[which])
+            for idx in np.ndindex(base[which].shape):
+                loss = []
+                for sgn in (1.0, -1.0):
+                    xs = [x.copy() for x in base]
+                    xs[which][idx] += sgn * h
+                    o, _ = orc.attention_forward_sparse(*xs, 0.45, causal, m, block=4)
+                    loss.append(np.sum(o * do))
+                num[idx] = (loss[0] - loss[1]) / (2 * h)
+            err = np.max(np.abs(num - grads[which])) / max(1.0, np.max(np.abs(num)))
+            assert err < 1e-7, f"sparse finite differences grad {which} causal={causal}: {err:.2e}"
+
+
 ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pin_constant_v,
             pin_q_zero, pin_causal_row0_and_n1, pin_shift_invariance, pin_permutation,
             pin_online_recurrence, pin_scipy_logsumexp, pin_torch_autograd,
             pin_finite_differences, pin_backward_invariants,
             pin_kv_reduces_to_square, pin_kv_worked_example, pin_kv_bruteforce, pin_kv_decode_and_empty,
-            pin_kv_padding_invariance, pin_kv_torch_autograd, pin_kv_finite_differences]
+            pin_kv_padding_invariance, pin_kv_torch_autograd, pin_kv_finite_differences,
+            pin_sparse_all_ones_is_dense, pin_sparse_bruteforce, pin_sparse_block_diagonal,
+            pin_sparse_torch_autograd, pin_sparse_finite_differences]

@@ -42,6 +42,12 @@ MUTANTS = {
     "kv padding rows not zero": ("o = np.zeros(q.shape[:3] + (v.shape[3],))", "o = np.ones(q.shape[:3] + (v.shape[3],))"),
     "kv empty rows weighted": ("p[seen] = e[seen] / l[seen, None]", "p = e / np.maximum(l, 1e-300)[:, None] + (~seen)[:, None]"),
     "kv dQ missing scale": ("dq[b, h, :a] = scale * (ds @ kh)", "dq[b, h, :a] = (ds @ kh)"),
+    "sparse mask transposed": ("return np.asarray(mask_bh, dtype=bool)[idx[:, None], idx[None, :]]",
+                               "return np.asarray(mask_bh, dtype=bool).T[idx[:, None], idx[None, :]]"),
+    "sparse block size off by one": ("idx = np.arange(n) // block", "idx = np.arange(n) // (block + 1)"),
+    "sparse mask ignored in backward": ("            s = np.where(_block_visible(bm[b, h], N, block), s, -np.inf)\n            p, _ = ",
+                                        "            p, _ = "),
+    "sparse dV not transposed": ("dv[b, h] = p.T @ do[b, h]", "dv[b, h] = p @ do[b, h]"),
     "kv dropped D term": ("ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))\n            dq[b, h, :a]",
                           "ds = p * dp\n            dq[b, h, :a]"),
 }
