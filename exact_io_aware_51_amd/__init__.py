@@ -1,9 +1,10 @@
 """Python binding of libfa, the gfx950 fused exact-attention library.
 
 The functions named like the C entry points (fa_fwd, fa_bwd, fa_fwd_kv,
-fa_bwd_kv, fa_bwd_workspace_bytes, fa_status_string, fa_version, ...) take raw
+fa_bwd_kv, fa_fwd_sparse, fa_bwd_sparse, fa_bwd_workspace_bytes, ...) take raw
 device addresses and sizes exactly as include/fa.h declares them.  forward(),
-backward(), forward_kv() and backward_kv() are conveniences for torch tensors:
+backward(), forward_kv(), backward_kv(), forward_sparse() and
+backward_sparse() are conveniences for torch tensors:
 they check shapes, allocate the outputs with torch, pass data_ptr()s and
 torch's current HIP stream, and raise FaError on a non-zero status.  All
 arithmetic happens in the HIP kernels; there is no CPU or PyTorch fallback,
@@ -16,17 +17,19 @@ import math
 import os
 
 __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_status_string",
-           "fa_version", "forward", "backward", "forward_kv", "backward_kv", "library_path", "load"]
+           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
+           "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
+           "backward_kv", "forward_sparse", "backward_sparse", "SPARSE_BLOCK", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+SPARSE_BLOCK = 128  # rows and keys per block of a block-sparse mask (FA_SPARSE_BLOCK)
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_fwd_kv", "fa_bwd_kv", "fa_status_string", "fa_version")
+           "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -64,6 +67,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kv.restype = i
     lib.fa_bwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, vp, vp, f, i, i, vp]
     lib.fa_bwd_kv.restype = i
+    lib.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, f, i, i, vp]
+    lib.fa_fwd_sparse.restype = i
+    lib.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, vp, f, i, i, vp]
+    lib.fa_bwd_sparse.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -109,6 +116,16 @@ def fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, 
               seqlens_k, scale, causal, dtype, stream) -> int:
     return load().fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, Nq, Nk, d,
                             seqlens_q, seqlens_k, scale, causal, dtype, stream)
+
+
+def fa_fwd_sparse(q, k, v, o, lse, B, H, N, d, block_mask, scale, causal, dtype, stream) -> int:
+    return load().fa_fwd_sparse(q, k, v, o, lse, B, H, N, d, block_mask, scale, causal, dtype, stream)
+
+
+def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, block_mask,
+                  scale, causal, dtype, stream) -> int:
+    return load().fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                                block_mask, scale, causal, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
@@ -254,4 +271,50 @@ def backward_kv(q, k, v, o, lse, dout, seqlens_q=None, seqlens_k=None, scale=Non
                    sk.data_ptr() if sk is not None else None, scale, int(bool(causal)), code, _stream(q, stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_kv")
+    return dq, dk, dv
+
+
+def _block_mask(m, B, H, N, device):
+    import torch
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if not isinstance(m, torch.Tensor) or m.device != device or m.dtype != torch.uint8:
+        raise ValueError("block_mask must be a uint8 tensor on the tensors' device")
+    if tuple(m.shape) != (B, H, nb, nb) or not m.is_contiguous():
+        raise ValueError(f"block_mask must be contiguous [B, H, {nb}, {nb}] (blocks of {SPARSE_BLOCK})")
+    return m
+
+
+def forward_sparse(q, k, v, block_mask, scale=None, causal=False, need_lse=True, stream=None):
+    """fa_fwd_sparse on torch tensors: block_mask uint8 [B, H, nb, nb], 0 removes a 128 x 128 block."""
+    import torch
+    _check(q, k, v)
+    B, H, N, d = q.shape
+    m = _block_mask(block_mask, B, H, N, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if need_lse else None
+    st = fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr() if lse is not None else None, B, H, N, d, m.data_ptr(), scale,
+                       int(bool(causal)), _dtype_code(q), _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_sparse")
+    return o, lse
+
+
+def backward_sparse(q, k, v, o, lse, dout, block_mask, scale=None, causal=False, stream=None):
+    """fa_bwd_sparse on torch tensors (o and lse from forward_sparse with the same mask)."""
+    import torch
+    _check(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    m = _block_mask(block_mask, B, H, N, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_bytes(B, H, N, d, code)
+    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                       B, H, N, d, m.data_ptr(), scale, int(bool(causal)), code, _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_sparse")
     return dq, dk, dv

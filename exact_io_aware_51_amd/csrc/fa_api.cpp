@@ -13,6 +13,9 @@
 namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
+// Block-sparse kernels keep one mask row or column as bits in LDS: at most
+// 64 x 64 blocks of 128.
+constexpr int kMaxSparseN = 64 * 64 * 128;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -45,10 +48,17 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Bytes of a block-sparse mask: one byte per (128-query block, 128-key block) pair per (batch, head).
+size_t mask_bytes(int B, int H, int Nq, int Nk) {
+  const size_t bq = (size_t)(Nq + fa::kMaskBlock - 1) / fa::kMaskBlock, bk = (size_t)(Nk + fa::kMaskBlock - 1) / fa::kMaskBlock;
+  return (size_t)B * H * bq * bk;
+}
+
 // Forward validation and launch for q/o of Nq rows and k/v of Nk rows per
 // (batch, head), with optional device arrays of per-sequence lengths.
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
-            const int* seqlens_q, const int* seqlens_k, float scale, int causal, int dtype, void* stream) {
+            const int* seqlens_q, const int* seqlens_k, const unsigned char* block_mask, float scale, int causal,
+            int dtype, void* stream) {
   int st = check_shape(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
@@ -59,7 +69,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   const size_t tk = (size_t)B * H * Nk * d * elem_bytes(dtype);
   const size_t lb = (size_t)B * H * Nq * sizeof(float);
   const size_t sb = (size_t)B * sizeof(int);
-  const Range ins[5] = {{q, tq}, {k, tk}, {v, tk}, {seqlens_q, seqlens_q ? sb : 0}, {seqlens_k, seqlens_k ? sb : 0}};
+  const Range ins[6] = {{q, tq}, {k, tk}, {v, tk}, {seqlens_q, seqlens_q ? sb : 0}, {seqlens_k, seqlens_k ? sb : 0},
+                        {block_mask, block_mask ? mask_bytes(B, H, Nq, Nk) : 0}};
   for (const Range& r : ins) {
     if (overlap({o, tq}, r)) return FA_ERR_INVALID_ARG;
     if (lse && overlap({lse, lb}, r)) return FA_ERR_INVALID_ARG;
@@ -70,6 +81,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk; p.d = d;
   p.seqlens_q = seqlens_q; p.seqlens_k = seqlens_k;
+  p.block_mask = block_mask;
   p.scale = scale; p.causal = causal; p.dtype = dtype;
   (void)hipGetLastError();  // report only this launch's error
   return hip_status(fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream)));
@@ -94,12 +106,19 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, fa_dtype dtype, void* stream) {
-  return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype, stream);
+  return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, stream);
 }
 
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
               const int* seqlens_q, const int* seqlens_k, float scale, int causal, fa_dtype dtype, void* stream) {
-  return run_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, (int)dtype, stream);
+  return run_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype, stream);
+}
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                  const unsigned char* block_mask, float scale, int causal, fa_dtype dtype, void* stream) {
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  if (N > kMaxSparseN) return FA_ERR_UNSUPPORTED;
+  return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
@@ -124,7 +143,7 @@ const char kUnusedTag = 0;
 const void* const kUnused = &kUnusedTag;
 
 int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d, const int* seqlens_q,
-              const int* seqlens_k, float scale, int causal, int dtype) {
+              const int* seqlens_k, const unsigned char* block_mask, float scale, int causal, int dtype) {
   int st = check_shape(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if ((seqlens_q && !aligned(seqlens_q, 4)) || (seqlens_k && !aligned(seqlens_k, 4))) return FA_ERR_INVALID_ARG;
@@ -140,8 +159,9 @@ int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int Nq, in
   const size_t tk = (size_t)B * H * Nk * d * elem_bytes(dtype);
   const size_t lb = (size_t)B * H * Nq * sizeof(float);
   const size_t sb = (size_t)B * sizeof(int);
-  const Range ins[8] = {{p.q, tq},    {p.k, tk},   {p.v, tk}, {p.o, tq}, {p.dout, tq}, {p.lse, lb},
-                        {seqlens_q ? seqlens_q : kUnused, sb}, {seqlens_k ? seqlens_k : kUnused, sb}};
+  const Range ins[9] = {{p.q, tq},    {p.k, tk},   {p.v, tk}, {p.o, tq}, {p.dout, tq}, {p.lse, lb},
+                        {seqlens_q ? seqlens_q : kUnused, sb}, {seqlens_k ? seqlens_k : kUnused, sb},
+                        {block_mask ? static_cast<const void*>(block_mask) : kUnused, mask_bytes(B, H, Nq, Nk)}};
   const Range outs[4] = {{p.dq, tq}, {p.dk, tk}, {p.dv, tk}, {p.ws, need}};
   for (int i = 0; i < 4; ++i) {
     if (outs[i].p == kUnused) continue;
@@ -154,7 +174,8 @@ int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int Nq, in
 }
 
 fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d, const int* seqlens_q,
-                          const int* seqlens_k, float scale, int causal, int dtype) {
+                          const int* seqlens_k, const unsigned char* block_mask, float scale, int causal,
+                          int dtype) {
   fa::BwdProblem b;
   auto use = [](const void* x) { return x == kUnused ? nullptr : x; };
   b.q = use(p.q); b.k = use(p.k); b.v = use(p.v); b.o = use(p.o); b.dout = use(p.dout);
@@ -163,6 +184,7 @@ fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d
   b.dvec = static_cast<float*>(p.ws);
   b.B = B; b.H = H; b.Nq = Nq; b.Nk = Nk; b.d = d;
   b.seqlens_q = seqlens_q; b.seqlens_k = seqlens_k;
+  b.block_mask = block_mask;
   b.scale = scale; b.causal = causal; b.dtype = dtype;
   return b;
 }
@@ -182,9 +204,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
            float scale, int causal, fa_dtype dtype, void* stream) {
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
-  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype), 0, 2, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), 0, 2, stream);
 }
 
 int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -192,18 +214,31 @@ int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const 
               int d, const int* seqlens_q, const int* seqlens_k, float scale, int causal, fa_dtype dtype,
               void* stream) {
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
-  int st = check_bwd(p, workspace_bytes, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, (int)dtype), 0, 2, stream);
+  return run_stages(bwd_problem(p, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype), 0, 2,
+                    stream);
+}
+
+int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                  const unsigned char* block_mask, float scale, int causal, fa_dtype dtype, void* stream) {
+  if (!block_mask) return FA_ERR_INVALID_ARG;
+  if (N > kMaxSparseN) return FA_ERR_UNSUPPORTED;
+  const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype), 0, 2,
+                    stream);
 }
 
 int fa_bwd_rowsum(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B, int H, int N,
                   int d, fa_dtype dtype, void* stream) {
   void* un = const_cast<void*>(kUnused);
   const BwdPtrs p{kUnused, kUnused, kUnused, o, dout, kUnused, un, un, un, workspace};
-  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, 1.0f, 0, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, 1.0f, 0, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, 1.0f, 0, (int)dtype), 0, 0, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, 1.0f, 0, (int)dtype), 0, 0, stream);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -211,9 +246,9 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
                 float scale, int causal, fa_dtype dtype, void* stream) {
   void* un = const_cast<void*>(kUnused);
   const BwdPtrs p{q, k, v, kUnused, dout, lse, un, dk, dv, const_cast<void*>(workspace)};
-  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype), 1, 1, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), 1, 1, stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, const void* workspace,
@@ -221,9 +256,9 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
               void* stream) {
   void* un = const_cast<void*>(kUnused);
   const BwdPtrs p{q, k, v, kUnused, dout, lse, dq, un, un, const_cast<void*>(workspace)};
-  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype);
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, scale, causal, (int)dtype), 2, 2, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), 2, 2, stream);
 }
 
 }  // extern "C"

@@ -36,6 +36,8 @@ struct BwdArgs {
   float* dvec;
   const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
   const int* seqlens_k;
+  const unsigned char* block_mask;  // block-sparse: [B, H, nbq, nbk] (SPARSE kernels only)
+  int nbq, nbk;
   int Nq, Nk, H;
   int nblk;    // blocks per head along the owned dimension
   int total;   // workgroups in the grid
@@ -45,6 +47,7 @@ struct BwdArgs {
 
 constexpr int kBwdThreads = 256;
 constexpr int kBwdOwn = 128;   // owned rows per workgroup (32 per wave)
+static_assert(kBwdOwn == kMaskBlock, "a workgroup's owned rows are one block-sparse mask block");
 constexpr int kBwdTile = 64;   // streamed rows per tile
 
 // --------------------------------------------------------------------------
@@ -86,7 +89,7 @@ struct BwdLayout {
 
 // --------------------------------------------------------------------------
 // dK, dV for 128 keys per workgroup.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using M = Mma<T>;
   using L = BwdLayout<T, D>;
@@ -139,6 +142,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int f = floor_div(kb0 - sq.off, kBwdTile);
     first = f > 0 ? f : 0;
   }
+  // block-sparse: a query tile is live unless its 128-row block is masked out for this key block
+  const unsigned char* mcol = SPARSE ? a.block_mask + (size_t)bh * a.nbq * a.nbk + kblk : nullptr;
+  auto live = [&](int j) {
+    if constexpr (SPARSE)
+      return mcol[(size_t)((j * kBwdTile) / kMaskBlock) * a.nbk] != 0;
+    else
+      return true;
+  };
 
   u32x4 qreg[L::PER_THREAD], doreg[L::PER_THREAD];
   float lse_r = 0.0f, d_r = 0.0f;
@@ -196,10 +207,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   for (int j = first; j < ntiles; ++j) {
     const int buf = (j - first) & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    if (j + 1 < ntiles && live(j + 1)) load_tile(j + 1);
     const int i0 = j * kBwdTile;
-    // waves whose keys all follow this tile's last query have nothing to do
-    if (!CAUSAL || i0 + kBwdTile - 1 + sq.off >= kw) {
+    // waves whose keys all follow this tile's last query have nothing to do,
+    // and neither does anyone for a tile block sparsity removed
+    if ((!CAUSAL || i0 + kBwdTile - 1 + sq.off >= kw) && live(j)) {
       const T* qt = lds_q + buf * L::TILE;
       const T* dot = lds_do + buf * L::TILE;
       const float* lt = lds_lse + buf * kBwdTile;
@@ -275,7 +287,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // --------------------------------------------------------------------------
 // dQ for 128 queries per workgroup.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using M = Mma<T>;
   using L = BwdLayout<T, D>;
@@ -320,6 +332,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   query_block_tiles<CAUSAL, kBwdTile>(sq, q0, kBwdOwn, &ntiles, &nfull);
   const int lim = key_limit<CAUSAL>(sq, myq);
   const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
+  // block-sparse: a key tile is live unless its 128-key block is masked out for this query block
+  const unsigned char* mrow = SPARSE ? a.block_mask + ((size_t)bh * a.nbq + qb) * a.nbk : nullptr;
+  auto live = [&](int j) {
+    if constexpr (SPARSE)
+      return mrow[(j * kBwdTile) / kMaskBlock] != 0;
+    else
+      return true;
+  };
 
   u32x4 kreg[L::PER_THREAD], vreg[L::PER_THREAD];
   auto load_tile = [&](int j) {
@@ -363,9 +383,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    if (j + 1 < ntiles && live(j + 1)) load_tile(j + 1);
     const int k0 = j * kBwdTile;
-    if (!CAUSAL || k0 <= wlast) {
+    if ((!CAUSAL || k0 <= wlast) && live(j)) {
       const T* kt = lds_k + buf * L::TILE;
       const T* vt = lds_v + buf * L::TILE;
       // unmasked when every row of the wave may see every key of the tile
@@ -423,7 +443,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t stream) {
   if (stage == 0) {
     const long long rows = (long long)p.B * p.H * p.Nq;
@@ -438,22 +458,31 @@ static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t strea
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.dout = p.dout; a.lse = p.lse;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.dvec = p.dvec;
   a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.block_mask = p.block_mask;
+  a.nbq = (p.Nq + kMaskBlock - 1) / kMaskBlock;
+  a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
   a.nblk = ((stage == 1 ? p.Nk : p.Nq) + kBwdOwn - 1) / kBwdOwn;
   a.total = a.nblk * p.B * p.H;
   if (stage == 1)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, bool SPARSE>
+static hipError_t launch_bwd_s(const BwdProblem& p, int stage, hipStream_t s) {
+  if (p.d == 64)
+    return p.causal ? launch_bwd_t<T, 64, true, SPARSE>(p, stage, s) : launch_bwd_t<T, 64, false, SPARSE>(p, stage, s);
+  return p.causal ? launch_bwd_t<T, 128, true, SPARSE>(p, stage, s) : launch_bwd_t<T, 128, false, SPARSE>(p, stage, s);
 }
 
 template <typename T>
 static hipError_t launch_bwd_d(const BwdProblem& p, int stage, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_bwd_t<T, 64, true>(p, stage, s) : launch_bwd_t<T, 64, false>(p, stage, s);
-  return p.causal ? launch_bwd_t<T, 128, true>(p, stage, s) : launch_bwd_t<T, 128, false>(p, stage, s);
+  return p.block_mask != nullptr ? launch_bwd_s<T, true>(p, stage, s) : launch_bwd_s<T, false>(p, stage, s);
 }
 
 #ifndef FA_DQ16

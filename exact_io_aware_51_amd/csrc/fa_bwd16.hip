@@ -31,6 +31,8 @@ struct Bwd16Args {
   void* dv;
   const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
   const int* seqlens_k;
+  const unsigned char* block_mask;  // block-sparse: [B, H, nbq, nbk] (SPARSE kernels only)
+  int nbq, nbk;
   int Nq, Nk, H;
   int nblk;
   int total;
@@ -72,7 +74,7 @@ __device__ inline void reads_ahead() {
 #define FA_DQ_OCC128 1
 #endif
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(Bwd16Args a) {
   using M = Mma<T>;
   using TL = Tile16<D>;
@@ -118,10 +120,17 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
   query_block_tiles<CAUSAL, 64>(sq, q0, 128, &nt, &nt_full);
   const int lim = key_limit<CAUSAL>(sq, myq);
   const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
+  // block-sparse: this query block's mask row, packed into bits in LDS; a key
+  // tile is live unless its 128-key block is masked out
+  __shared__ uint64_t mwords[SPARSE ? kMaxMaskWords : 1];
+  if constexpr (SPARSE) {
+    pack_mask_words(mwords, a.block_mask + ((size_t)bh * a.nbq + qb) * a.nbk, a.nbk, 1, lane, wave, 4);
+    __syncthreads();
+  }
 
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D>(goff, wave, lane);
-  auto dma = [&](const char* g, int row0, int region) {
+  auto dma = [&](const char* g, int row0, int region) __attribute__((always_inline)) {
     const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i) lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
     for (int t = 0; t < 2; ++t) dsf[kb][t] = zero_frag<T>();
   const float c = a.c;
 
-  auto dq_prev = [&](auto kps) {
+  auto dq_prev = [&](auto kps) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -162,20 +171,22 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
 #endif
   };
 
-  // Step j: K_j in K stage ks3 = j % 3, V_j in V stage vs2 = j % 2, K_{j-1} in (j - 1) % 3.
-  auto step = [&](int j, auto ks3, auto vs2, auto full_tag) {
+  // Step j (jp: the tile visited before it, jn: the one after; j - 1 and j + 1
+  // unless block sparsity skips tiles): K_j in K stage ks3, V_j in V stage vs2,
+  // K_jp in the K stage before ks3.  Stages advance by one per step.
+  auto step = [&](int j, int jn, int jp, auto ks3, auto vs2, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int kps = ks3 == 0 ? 2 : ks3 - 1;
     wait_vmem();
     __builtin_amdgcn_s_barrier();
-    if (j + 1 < nt) {
+    if (jn < nt) {
       const int kn = ks3 == 2 ? 0 : ks3 + 1;
-      dma(Kg, 64 * (j + 1), KREG + kn * TL::BYTES);
-      dma(Vg, 64 * (j + 1), VREG + (vs2 ^ 1) * TL::BYTES);
+      dma(Kg, 64 * jn, KREG + kn * TL::BYTES);
+      dma(Vg, 64 * jn, VREG + (vs2 ^ 1) * TL::BYTES);
     }
     const int k0 = 64 * j;
     const bool act = FULL || !CAUSAL || k0 <= wlast;
-    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - 64 <= wlast));
+    const bool prev = FULL || (jp >= 0 && (!CAUSAL || 64 * jp <= wlast));
     if (act) {
       const int t0 = lim - k0 - 4 * h;
       // the two 32-key halves one after the other keeps two accumulators live, not four
@@ -219,31 +230,58 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
-    dma(Kg, 0, KREG);
-    dma(Vg, 0, VREG);
-    // tile 0 owes no dQ product yet: generic step
-    step(0, 0, 0, std::false_type{});
-    int j = 1;
-    // mask-free steps, six at a time so that every LDS offset is a constant
-    for (; j + 5 < nt_full; j += 6) {
-      step(j, I1{}, I1{}, std::true_type{});
-      step(j + 1, I2{}, I0{}, std::true_type{});
-      step(j + 2, I0{}, I1{}, std::true_type{});
-      step(j + 3, I1{}, I0{}, std::true_type{});
-      step(j + 4, I2{}, I1{}, std::true_type{});
-      step(j + 5, I0{}, I0{}, std::true_type{});
+  if constexpr (!SPARSE) {
+    if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
+      dma(Kg, 0, KREG);
+      dma(Vg, 0, VREG);
+      // tile 0 owes no dQ product yet: generic step
+      step(0, 1, -1, 0, 0, std::false_type{});
+      int j = 1;
+      // mask-free steps, six at a time so that every LDS offset is a constant
+      for (; j + 5 < nt_full; j += 6) {
+        step(j, j + 1, j - 1, I1{}, I1{}, std::true_type{});
+        step(j + 1, j + 2, j, I2{}, I0{}, std::true_type{});
+        step(j + 2, j + 3, j + 1, I0{}, I1{}, std::true_type{});
+        step(j + 3, j + 4, j + 2, I1{}, I0{}, std::true_type{});
+        step(j + 4, j + 5, j + 3, I2{}, I1{}, std::true_type{});
+        step(j + 5, j + 6, j + 4, I0{}, I0{}, std::true_type{});
+      }
+      // the rest (up to five mask-free tiles, then the masked ones): runtime stages
+      for (; j < nt; ++j) {
+        if (j < nt_full)
+          step(j, j + 1, j - 1, j % 3, j & 1, std::true_type{});
+        else
+          step(j, j + 1, j - 1, j % 3, j & 1, std::false_type{});
+      }
+      wait_vmem();
+      __builtin_amdgcn_s_barrier();
+      if (!CAUSAL || 64 * (nt - 1) <= wlast) dq_prev((nt - 1) % 3);
     }
-    // the rest (up to five mask-free tiles, then the masked ones): runtime stages
-    for (; j < nt; ++j) {
-      if (j < nt_full)
-        step(j, j % 3, j & 1, std::true_type{});
-      else
-        step(j, j % 3, j & 1, std::false_type{});
+  } else {
+    // Only live tiles are visited, in increasing order; step t uses K stage
+    // t % 3 and V stage t % 2, and is unmasked when its tile lies below nt_full.
+    auto next = [&](int j) __attribute__((always_inline)) { return next_live_tile(mwords, j, 2, a.nbk, nt); };
+    int j = next(-1);
+    if (j < nt) {
+      dma(Kg, 64 * j, KREG);
+      dma(Vg, 64 * j, VREG);
+      int jn = next(j);
+      step(j, jn, -1, 0, 0, std::false_type{});
+      int jp = j, t = 1;
+      j = jn;
+      for (; j < nt; ++t) {
+        jn = next(j);
+        if (j < nt_full)
+          step(j, jn, jp, t % 3, t & 1, std::true_type{});
+        else
+          step(j, jn, jp, t % 3, t & 1, std::false_type{});
+        jp = j;
+        j = jn;
+      }
+      wait_vmem();
+      __builtin_amdgcn_s_barrier();
+      if (!CAUSAL || 64 * jp <= wlast) dq_prev((t - 1) % 3);
     }
-    wait_vmem();
-    __builtin_amdgcn_s_barrier();
-    if (!CAUSAL || 64 * (nt - 1) <= wlast) dq_prev((nt - 1) % 3);
   }
 
   if (myq < Nq) {  // padding rows store zeros
@@ -272,7 +310,7 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
 // The four accumulators (dK^T, dV^T) and the stationary fragments need about
 // 280 VGPRs, so one wave per SIMD runs this kernel; the element-wise work of
 // one half overlaps the matrix ops of the other inside the wave.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
   using M = Mma<T>;
   using TL = Tile16<D>;
@@ -329,11 +367,18 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
     full0 = g > first ? g : first;
   }
   const int full1 = sq.lq / 64;
+  // block-sparse: this key block's mask column, packed into bits in LDS; a
+  // query tile is live unless its 128-row block is masked out
+  __shared__ uint64_t mwords[SPARSE ? kMaxMaskWords : 1];
+  if constexpr (SPARSE) {
+    pack_mask_words(mwords, a.block_mask + (size_t)bh * a.nbq * a.nbk + kblk, a.nbq, a.nbk, lane, wave, 4);
+    __syncthreads();
+  }
 
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D>(goff, wave, lane);
   float lse_next = 0.0f, d_next = 0.0f;  // wave 0 stages the next tile's per-row values
-  auto fetch = [&](int i, int stage) {
+  auto fetch = [&](int i, int stage) __attribute__((always_inline)) {
     const int row0 = 64 * i;
     const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lq - row0) * TL::ROWB);
     const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lq - row0) * TL::ROWB);
@@ -348,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
       d_next = qi < sq.lq ? dvec[qi] : 0.0f;
     }
   };
-  auto publish = [&](int stage) {  // wave 0 writes the staged per-row values
+  auto publish = [&](int stage) __attribute__((always_inline)) {  // wave 0 writes the staged per-row values
     if (wave == 0) {
       reinterpret_cast<float*>(smem + LREG)[stage * 64 + lane] = lse_next;
       reinterpret_cast<float*>(smem + DREG)[stage * 64 + lane] = d_next;
@@ -371,14 +416,15 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
   }
   const float c = a.c;
 
-  // Step i: query tile i in stage st; the next tile is fetched into st ^ 1.
-  auto step = [&](int i, auto st, auto full_tag) {
+  // Step i: query tile i in stage st; the next tile to visit, in (i + 1 unless
+  // block sparsity skips tiles), is fetched into st ^ 1.
+  auto step = [&](int i, int in, auto st, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
     wait_vmem();
     publish(st);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS writes done (lgkmcnt(0))
     __builtin_amdgcn_s_barrier();
-    if (i + 1 < nt) fetch(i + 1, st ^ 1);
+    if (in < nt) fetch(in, st ^ 1);
     const int i0 = 64 * i;
     if (!FULL && CAUSAL && i0 + 63 + sq.off < kw) return;  // no query of the tile sees this wave's keys
     const int qo = QREG + st * TL::BYTES, oo = OREG + st * TL::BYTES;
@@ -437,31 +483,57 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  if (first < nt) {
-    fetch(first, 0);
-    int i = first;
-    for (; i < nt && i < full0; ++i) {
-      if ((i - first) & 1)
-        step(i, I1{}, std::false_type{});
-      else
-        step(i, I0{}, std::false_type{});
-    }
-    // mask-free tiles, two at a time (constant LDS offsets)
-    for (; i + 1 < full1; i += 2) {
-      if ((i - first) & 1) {
-        step(i, I1{}, std::true_type{});
-        step(i + 1, I0{}, std::true_type{});
-      } else {
-        step(i, I0{}, std::true_type{});
-        step(i + 1, I1{}, std::true_type{});
+  if constexpr (!SPARSE) {
+    if (first < nt) {
+      fetch(first, 0);
+      int i = first;
+      for (; i < nt && i < full0; ++i) {
+        if ((i - first) & 1)
+          step(i, i + 1, I1{}, std::false_type{});
+        else
+          step(i, i + 1, I0{}, std::false_type{});
+      }
+      // mask-free tiles, two at a time (constant LDS offsets)
+      for (; i + 1 < full1; i += 2) {
+        if ((i - first) & 1) {
+          step(i, i + 1, I1{}, std::true_type{});
+          step(i + 1, i + 2, I0{}, std::true_type{});
+        } else {
+          step(i, i + 1, I0{}, std::true_type{});
+          step(i + 1, i + 2, I1{}, std::true_type{});
+        }
+      }
+      for (; i < nt; ++i) {
+        const bool full = i < full1;
+        if ((i - first) & 1) {
+          if (full) step(i, i + 1, I1{}, std::true_type{}); else step(i, i + 1, I1{}, std::false_type{});
+        } else {
+          if (full) step(i, i + 1, I0{}, std::true_type{}); else step(i, i + 1, I0{}, std::false_type{});
+        }
       }
     }
-    for (; i < nt; ++i) {
-      const bool full = i < full1;
-      if ((i - first) & 1) {
-        if (full) step(i, I1{}, std::true_type{}); else step(i, I1{}, std::false_type{});
-      } else {
-        if (full) step(i, I0{}, std::true_type{}); else step(i, I0{}, std::false_type{});
+  } else {
+    // Only live query tiles are visited, in increasing order, alternating
+    // stages; a step is unmasked when its tile lies in [full0, full1).
+    auto next = [&](int i) __attribute__((always_inline)) { return next_live_tile(mwords, i, 2, a.nbq, nt); };
+    auto visit = [&](int i, int in, auto st) __attribute__((always_inline)) {
+      if (full0 <= i && i < full1)
+        step(i, in, st, std::true_type{});
+      else
+        step(i, in, st, std::false_type{});
+    };
+    int i = live_tile_from(mwords, first, 2, a.nbq, nt);
+    if (i < nt) {
+      fetch(i, 0);
+      while (true) {
+        int in = next(i);
+        visit(i, in, I0{});
+        i = in;
+        if (i >= nt) break;
+        in = next(i);
+        visit(i, in, I1{});
+        i = in;
+        if (i >= nt) break;
       }
     }
   }
@@ -488,54 +560,62 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
-static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
+// Fill the kernel arguments shared by the dK/dV and dQ kernels; nblk is the
+// number of owned 128-row blocks per (batch, head).
+static Bwd16Args bwd16_args(const BwdProblem& p, int nblk) {
   Bwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
   a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
+  a.block_mask = p.block_mask;
+  a.nbq = (p.Nq + kMaskBlock - 1) / kMaskBlock;
+  a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
-  a.nblk = (p.Nk + 127) / 128;
+  a.nblk = nblk;
   a.total = a.nblk * p.B * p.H;
-  hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  return a;
+}
+static_assert(kMaskBlock == 128, "a dK/dV workgroup's 128 keys are one mask block column");
+
+template <typename T, int D, bool CAUSAL, bool SPARSE>
+static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
+  const Bwd16Args a = bwd16_args(p, (p.Nk + 127) / 128);
+  hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_dkdv16_d(const BwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_dkdv16_t<T, 64, true>(p, s) : launch_dkdv16_t<T, 64, false>(p, s);
-  return p.causal ? launch_dkdv16_t<T, 128, true>(p, s) : launch_dkdv16_t<T, 128, false>(p, s);
+template <typename T, bool SPARSE>
+static hipError_t launch_dkdv16_s(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64)
+    return p.causal ? launch_dkdv16_t<T, 64, true, SPARSE>(p, s) : launch_dkdv16_t<T, 64, false, SPARSE>(p, s);
+  return p.causal ? launch_dkdv16_t<T, 128, true, SPARSE>(p, s) : launch_dkdv16_t<T, 128, false, SPARSE>(p, s);
 }
 
 hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s) {
-  return p.dtype == 1 ? launch_dkdv16_d<_Float16>(p, s) : launch_dkdv16_d<__bf16>(p, s);
+  if (p.dtype == 1)
+    return p.block_mask ? launch_dkdv16_s<_Float16, true>(p, s) : launch_dkdv16_s<_Float16, false>(p, s);
+  return p.block_mask ? launch_dkdv16_s<__bf16, true>(p, s) : launch_dkdv16_s<__bf16, false>(p, s);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_dq16_t(const BwdProblem& p, hipStream_t stream) {
-  Bwd16Args a;
-  a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
-  a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
-  a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
-  a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
-  a.scale = p.scale;
-  a.c = p.scale * kLog2e;
-  a.nblk = (p.Nq + 127) / 128;
-  a.total = a.nblk * p.B * p.H;
-  hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  const Bwd16Args a = bwd16_args(p, (p.Nq + 127) / 128);
+  hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_dq16_d(const BwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_dq16_t<T, 64, true>(p, s) : launch_dq16_t<T, 64, false>(p, s);
-  return p.causal ? launch_dq16_t<T, 128, true>(p, s) : launch_dq16_t<T, 128, false>(p, s);
+template <typename T, bool SPARSE>
+static hipError_t launch_dq16_s(const BwdProblem& p, hipStream_t s) {
+  if (p.d == 64)
+    return p.causal ? launch_dq16_t<T, 64, true, SPARSE>(p, s) : launch_dq16_t<T, 64, false, SPARSE>(p, s);
+  return p.causal ? launch_dq16_t<T, 128, true, SPARSE>(p, s) : launch_dq16_t<T, 128, false, SPARSE>(p, s);
 }
 
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s) {
-  return p.dtype == 1 ? launch_dq16_d<_Float16>(p, s) : launch_dq16_d<__bf16>(p, s);
+  if (p.dtype == 1) return p.block_mask ? launch_dq16_s<_Float16, true>(p, s) : launch_dq16_s<_Float16, false>(p, s);
+  return p.block_mask ? launch_dq16_s<__bf16, true>(p, s) : launch_dq16_s<__bf16, false>(p, s);
 }
 
 }  // namespace fa

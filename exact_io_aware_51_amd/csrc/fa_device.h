@@ -228,6 +228,63 @@ __device__ inline Seq seq_of(const int* seqlens_q, const int* seqlens_k, int b, 
   return {lq, lk, lk - lq};
 }
 
+// Block-sparse masks: one row (or column) of a [nbq, nbk] byte mask packed into
+// 64-bit words in LDS, bit b of word w standing for block 64 w + b.  Up to
+// kMaxMaskWords words, i.e. 4096 blocks per row or column.
+constexpr int kMaxMaskWords = 64;
+
+// Every wave of the workgroup packs words wave, wave + nwaves, ...: lane l of
+// word w reads mask[(64 w + l) * stride].  A barrier must follow before the
+// words are read.
+__device__ inline void pack_mask_words(uint64_t* words, const unsigned char* mask, int nb, int stride, int lane,
+                                       int wave, int nwaves) {
+  const int nw = (nb + 63) >> 6;
+  for (int w = wave; w < nw; w += nwaves) {
+    const int b = 64 * w + lane;
+    const bool on = b < nb && mask[(size_t)b * stride] != 0;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(on);
+    if (lane == 0) words[w] = bits;
+  }
+}
+
+// The first kept block at or after b (nb when there is none); wave-uniform.
+__device__ inline int next_kept(const uint64_t* words, int b, int nb) {
+  while (b < nb) {
+    const int w = b >> 6;
+    const uint64_t word = words[w];
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)word);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(word >> 32));
+    const uint64_t bits = ((((uint64_t)hi) << 32) | lo) >> (b & 63);
+    if (bits != 0) {
+      const int r = b + __builtin_ctzll(bits);
+      return r < nb ? r : nb;
+    }
+    b = (w + 1) << 6;
+  }
+  return nb;
+}
+
+// Tiles of kMaskBlock / tpb rows, n of them: a tile is live when its mask
+// block is kept.  The first live tile at or after t (n when there is none).
+__device__ inline int live_tile_from(const uint64_t* words, int t, int tpb, int nb, int n) {
+  if (t >= n) return n;
+  const int b = t / tpb;
+  const int kb = next_kept(words, b, nb);
+  if (kb == b) return t;
+  const int u = kb * tpb;
+  return u < n ? u : n;
+}
+
+// The live tile after the live tile t (or the first one, t = -1): the tiles of
+// one block are consecutive, so the next tile is live too unless it starts a
+// new block.
+__device__ inline int next_live_tile(const uint64_t* words, int t, int tpb, int nb, int n) {
+  const int u = t + 1;
+  if (u >= n) return n;
+  if (t >= 0 && u % tpb != 0) return u;
+  return live_tile_from(words, u, tpb, nb, n);
+}
+
 // Largest key query row i may see; negative when it sees none (a padding row,
 // or a causal row that starts before the first key).
 template <bool CAUSAL>

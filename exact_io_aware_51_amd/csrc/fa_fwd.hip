@@ -33,6 +33,8 @@ struct FwdArgs {
   float* lse;
   const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
   const int* seqlens_k;
+  const unsigned char* block_mask;  // block-sparse: [B, H, nqb, nbk] (SPARSE kernels only)
+  int nbk;
   int Nq, Nk, H;
   int nqb;     // query blocks per head
   int total;   // workgroups in the grid
@@ -86,7 +88,7 @@ __device__ inline void interleave() {
   __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) void fwd_kernel(FwdArgs a) {
   using M = Mma<T>;
   using L = FwdLayout<T, D>;
@@ -131,6 +133,14 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   // largest key this lane's query may see (negative: none)
   const int lim = key_limit<CAUSAL>(sq, myq);
   const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
+  // block-sparse: a key tile is live unless its 128-key block is masked out for this query block
+  const unsigned char* mrow = SPARSE ? a.block_mask + ((size_t)bh * a.nqb + qb) * a.nbk : nullptr;
+  auto live = [&](int j) {
+    if constexpr (SPARSE)
+      return mrow[(j * kFwdBN) / kMaskBlock] != 0;
+    else
+      return true;
+  };
 
   // Global -> register staging of one K/V tile: 16-byte chunks, coalesced.
   // The buffer view of the tile ends at the sequence's last key, so reads
@@ -258,10 +268,11 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
 
   for (int j = 0; j < ntiles; ++j) {
     const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
+    if (j + 1 < ntiles && live(j + 1)) load_tile(j + 1);
     const int k0 = j * kFwdBN;
-    // waves whose rows all precede this tile's first key have nothing to do
-    if (!CAUSAL || k0 <= wlast) {
+    // waves whose rows all precede this tile's first key have nothing to do,
+    // and neither does anyone for a tile block sparsity removed
+    if ((!CAUSAL || k0 <= wlast) && live(j)) {
       const T* kt = lds_k + buf * L::KTILE;
       const T* vt = lds_v + buf * L::VTILE;
       // a tile is unmasked for the wave when every row of it may see every key
@@ -298,25 +309,33 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   FwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
   a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
+  a.block_mask = p.block_mask;
+  a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
   a.nqb = (p.Nq + kFwdBM - 1) / kFwdBM;
+  static_assert(kFwdBM == kMaskBlock, "one workgroup's query rows are one mask block row");
   a.total = a.nqb * p.B * p.H;
   const float sc = p.scale;
   a.negate = sc < 0.0f;
   a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL>), dim3(a.total), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(kFwdThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, bool SPARSE>
+static hipError_t launch_fwd_s(const FwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_fwd_t<T, 64, true, SPARSE>(p, s) : launch_fwd_t<T, 64, false, SPARSE>(p, s);
+  return p.causal ? launch_fwd_t<T, 128, true, SPARSE>(p, s) : launch_fwd_t<T, 128, false, SPARSE>(p, s);
 }
 
 template <typename T>
 static hipError_t launch_fwd_d(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_fwd_t<T, 64, true>(p, s) : launch_fwd_t<T, 64, false>(p, s);
-  return p.causal ? launch_fwd_t<T, 128, true>(p, s) : launch_fwd_t<T, 128, false>(p, s);
+  return p.block_mask != nullptr ? launch_fwd_s<T, true>(p, s) : launch_fwd_s<T, false>(p, s);
 }
 
 #ifndef FA_FWD16

@@ -43,6 +43,8 @@ struct Fwd16Args {
   float* lse;
   const int* seqlens_q;  // optional per-sequence lengths (device int32[B])
   const int* seqlens_k;
+  const unsigned char* block_mask;  // block-sparse: [B, H, nqb, nbk] (SPARSE kernels only)
+  int nbk;
   int Nq, Nk, H;
   int nqb;
   int total;
@@ -64,7 +66,7 @@ struct Fwd16Args {
 #define FA_FWD_BN64 64
 #endif
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   constexpr int BN = D == 64 ? FA_FWD_BN64 : 64;  // keys per tile
   constexpr int KB = BN / 32;                      // 32-key blocks per tile
@@ -108,11 +110,19 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   query_block_tiles<CAUSAL, BN>(sq, q0, 128, &nt, &nt_full);
   const int lim = key_limit<CAUSAL>(sq, myq);
   const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
+  // block-sparse: this query block's mask row, packed into bits in LDS; a key
+  // tile is live unless its 128-key block is masked out
+  constexpr int TPB = kMaskBlock / BN;  // key tiles per mask block
+  __shared__ uint64_t mwords[SPARSE ? kMaxMaskWords : 1];
+  if constexpr (SPARSE) {
+    pack_mask_words(mwords, a.block_mask + ((size_t)bh * a.nqb + qb) * a.nbk, a.nbk, 1, lane, wave, 4);
+    __syncthreads();
+  }
 
   // ---- direct loads: lane's source offset inside a tile, per round
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D, BN>(goff, wave, lane);
-  auto dma = [&](const char* g, int row0, int region) {
+  auto dma = [&](const char* g, int row0, int region) __attribute__((always_inline)) {
     const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i)
@@ -128,10 +138,10 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) vaddr[mb][hf] = VREG + tile16_tr_addr<D>(lane, mb, hf);
-  auto kfrag = [&](int stage, int kb, int ks) {
+  auto kfrag = [&](int stage, int kb, int ks) __attribute__((always_inline)) {
     return tile16_row_frag<T>(smem, kaddr[ks] + stage * TL::BYTES + kb * 32 * TL::ROWB);
   };
-  auto vfrag = [&](int stage, int kb, int t, int mb) {
+  auto vfrag = [&](int stage, int kb, int t, int mb) __attribute__((always_inline)) {
     return tile16_tr_frag<T, D>(smem, vaddr[mb][0], vaddr[mb][1], stage * TL::BYTES + (32 * kb + 16 * t) * TL::ROWB);
   };
 
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   float l = 0.0f;
   const float c = a.c;
 
-  auto pv = [&](int vstage) {
+  auto pv = [&](int vstage) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -156,19 +166,21 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
         for (int mb = 0; mb < MB; ++mb) oacc[mb] = M::mma(vfrag(vstage, kb, t, mb), pf[kb][t], oacc[mb]);
   };
 
-  // One pipeline step: S_j, softmax_j, and (if owed) O += P_{j-1} V_{j-1}.
-  // KST = j % 2 selects the stages: K_j in K stage KST, V_{j-1} in V stage KST^1.
-  auto step = [&](int j, auto kst_tag, auto full_tag) {
+  // One pipeline step: S_j, softmax_j, and (if owed) O += P_jp V_jp, where jp is
+  // the tile visited before j and jn the one visited after it (j - 1 and j + 1
+  // unless block sparsity skips tiles).  KST alternates from step to step: K_j
+  // sits in K stage KST, V_jp in V stage KST ^ 1.
+  auto step = [&](int j, int jn, int jp, auto kst_tag, auto full_tag) __attribute__((always_inline)) {
     constexpr int KST = decltype(kst_tag)::value;
-    constexpr bool FULL = decltype(full_tag)::value;  // unmasked, and tile j-1 was done
+    constexpr bool FULL = decltype(full_tag)::value;  // unmasked, and tile jp was done
     wait_vmem();
     __builtin_amdgcn_s_barrier();
-    if (j + 1 < nt) dma(Kg, BN * (j + 1), KREG + (KST ^ 1) * TL::BYTES);
+    if (jn < nt) dma(Kg, BN * jn, KREG + (KST ^ 1) * TL::BYTES);
     dma(Vg, BN * j, VREG + KST * TL::BYTES);
 
     const int k0 = BN * j;
     const bool act = FULL || !CAUSAL || k0 <= wlast;
-    const bool prev = FULL || (j > 0 && (!CAUSAL || k0 - BN <= wlast));
+    const bool prev = FULL || (jp >= 0 && (!CAUSAL || BN * jp <= wlast));
     if (act) {
 #if FA16_PRIO
       __builtin_amdgcn_s_setprio(1);
@@ -298,32 +310,78 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     }
   };
 
-  if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
-    dma(Kg, 0, KREG);
-    step(0, std::integral_constant<int, 0>{}, std::false_type{});
-    int j = 1;
-    for (; j + 1 < nt_full; j += 2) {
-      step(j, std::integral_constant<int, 1>{}, std::true_type{});
-      step(j + 1, std::integral_constant<int, 0>{}, std::true_type{});
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (!SPARSE) {
+    if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
+      dma(Kg, 0, KREG);
+      step(0, 1, -1, I0{}, std::false_type{});
+      int j = 1;
+      for (; j + 1 < nt_full; j += 2) {
+        step(j, j + 1, j - 1, I1{}, std::true_type{});
+        step(j + 1, j + 2, j, I0{}, std::true_type{});
+      }
+      if (j < nt_full) {
+        step(j, j + 1, j - 1, I1{}, std::true_type{});
+        ++j;
+      }
+      for (; j < nt; ++j) {
+        if (j & 1)
+          step(j, j + 1, j - 1, I1{}, std::false_type{});
+        else
+          step(j, j + 1, j - 1, I0{}, std::false_type{});
+      }
+      // the last tile's P still owes its V product
+      wait_vmem();
+      __builtin_amdgcn_s_barrier();
+      if (!CAUSAL || BN * (nt - 1) <= wlast) {
+        if ((nt - 1) & 1)
+          pv(1);
+        else
+          pv(0);
+      }
     }
-    if (j < nt_full) {
-      step(j, std::integral_constant<int, 1>{}, std::true_type{});
-      ++j;
-    }
-    for (; j < nt; ++j) {
-      if (j & 1)
-        step(j, std::integral_constant<int, 1>{}, std::false_type{});
-      else
-        step(j, std::integral_constant<int, 0>{}, std::false_type{});
-    }
-    // the last tile's P still owes its V product
-    wait_vmem();
-    __builtin_amdgcn_s_barrier();
-    if (!CAUSAL || BN * (nt - 1) <= wlast) {
-      if ((nt - 1) & 1)
-        pv(1);
-      else
-        pv(0);
+  } else {
+    // Only live tiles are visited; steps alternate stages as in the dense
+    // loop, and a step is unmasked when its tile (and so the previous one,
+    // visited in increasing order) lies below nt_full.
+    auto next = [&](int j) __attribute__((always_inline)) { return next_live_tile(mwords, j, TPB, a.nbk, nt); };
+    int j = next(-1);
+    if (j < nt) {
+      dma(Kg, BN * j, KREG);
+      int jp = -1, jn = next(j);
+      step(j, jn, jp, I0{}, std::false_type{});
+      jp = j; j = jn;
+      int par = 1;  // stage parity of the next step
+      while (j < nt_full) {
+        jn = next(j);
+        step(j, jn, jp, I1{}, std::true_type{});
+        jp = j; j = jn;
+        if (j >= nt_full) {
+          par = 0;
+          break;
+        }
+        jn = next(j);
+        step(j, jn, jp, I0{}, std::true_type{});
+        jp = j; j = jn;
+      }
+      for (; j < nt; par ^= 1) {
+        jn = next(j);
+        if (par)
+          step(j, jn, jp, I1{}, std::false_type{});
+        else
+          step(j, jn, jp, I0{}, std::false_type{});
+        jp = j; j = jn;
+      }
+      // the last visited tile's P still owes its V product (stage par ^ 1)
+      wait_vmem();
+      __builtin_amdgcn_s_barrier();
+      if (!CAUSAL || BN * jp <= wlast) {
+        if (par ^ 1)
+          pv(1);
+        else
+          pv(0);
+      }
     }
   }
 
@@ -348,25 +406,34 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   Fwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
   a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
+  a.block_mask = p.block_mask;
+  a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
   a.nqb = (p.Nq + 127) / 128;
+  static_assert(kMaskBlock == 128, "one workgroup's 128 query rows are one mask block row");
   a.total = a.nqb * p.B * p.H;
   const float sc = p.scale;
   a.negate = sc < 0.0f;
   a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename T, bool SPARSE>
+static hipError_t launch_fwd16_s(const FwdProblem& p, hipStream_t s) {
+  if (p.d == 64)
+    return p.causal ? launch_fwd16_t<T, 64, true, SPARSE>(p, s) : launch_fwd16_t<T, 64, false, SPARSE>(p, s);
+  return p.causal ? launch_fwd16_t<T, 128, true, SPARSE>(p, s) : launch_fwd16_t<T, 128, false, SPARSE>(p, s);
 }
 
 template <typename T>
 static hipError_t launch_fwd16_d(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_fwd16_t<T, 64, true>(p, s) : launch_fwd16_t<T, 64, false>(p, s);
-  return p.causal ? launch_fwd16_t<T, 128, true>(p, s) : launch_fwd16_t<T, 128, false>(p, s);
+  return p.block_mask != nullptr ? launch_fwd16_s<T, true>(p, s) : launch_fwd16_s<T, false>(p, s);
 }
 
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s) {

@@ -8,6 +8,8 @@ namespace fa {
 
 // q, o: [B, H, Nq, d]; k, v: [B, H, Nk, d]; lse: [B, H, Nq].  seqlens_q /
 // seqlens_k: optional device int32[B] sequence lengths (nullptr: Nq / Nk).
+constexpr int kMaskBlock = 128;  // rows and keys per block of a block-sparse mask
+
 struct FwdProblem {
   const void* q;
   const void* k;
@@ -17,6 +19,9 @@ struct FwdProblem {
   int B, H, Nq, Nk, d;
   const int* seqlens_q;
   const int* seqlens_k;
+  // optional device uint8 [B, H, ceil(Nq/128), ceil(Nk/128)]: 0 removes the
+  // scores of that (128-query block, 128-key block) pair (nullptr: dense)
+  const unsigned char* block_mask;
   float scale;
   int causal;
   int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
@@ -36,6 +41,7 @@ struct BwdProblem {
   int B, H, Nq, Nk, d;
   const int* seqlens_q;
   const int* seqlens_k;
+  const unsigned char* block_mask;  // as in FwdProblem
   float scale;
   int causal;
   int dtype;

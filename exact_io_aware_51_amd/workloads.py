@@ -106,3 +106,11 @@ def kv_inputs(B, H, Nq, Nk, d, dtype, seed, with_grad=True):
         out.append(torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32))
     dt = DTYPES[dtype]
     return tuple(x.to(dt) for x in out)
+
+
+def block_mask(B, H, N, keep, seed, block=128):
+    """uint8 [B, H, nb, nb] block mask, nb = ceil(N / block): each entry 1 with probability `keep`."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    nb = (N + block - 1) // block
+    return (torch.rand((B, H, nb, nb), generator=g) < keep).to(torch.uint8)

@@ -120,9 +120,9 @@ int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, con
               int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
 
 /*
- * Unequal query and key counts, and padded batches.  The pages apply causal
- * masking "for autoregressive decoding" and apply causal masking and padding
- * per tile ("How Flash Attention Works", sections "How Flash Attention Works:
+ * Unequal query and key counts, and padded batches.  The pages tie the causal
+ * mask to autoregressive decoding and apply causal masking and padding tile by
+ * tile ("How Flash Attention Works", sections "How Flash Attention Works:
  * The Exact-Attention Idea" and "Tiling Q, K, and V for Fast On-Chip
  * Memory"); they fix neither the causal alignment for unequal counts nor the
  * output of padding rows, and these entry points take the readings below.
@@ -158,6 +158,35 @@ int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o,
               int B, int H, int Nq, int Nk, int d,
               const int *seqlens_q, const int *seqlens_k,
               float scale, int causal, fa_dtype dtype, void *stream);
+
+/*
+ * Block-sparse attention.  The pages name a block-sparse extension studied
+ * beside the dense algorithm as a separate configuration ("FlashAttention"
+ * glossary entry, its definition) and fix no mask format; this one is:
+ *   block_mask : device pointer (not NULL; no alignment needed) to uint8
+ *                [B, H, nb, nb], nb = ceil(N / FA_SPARSE_BLOCK).  Entry
+ *                (b, h, i, j) = 0 removes the scores of query rows
+ *                [128 i, 128 i + 128) against keys [128 j, 128 j + 128);
+ *                any other value keeps them.  The causal mask, if set,
+ *                applies on top.  Removed tiles are skipped: not loaded, no
+ *                matrix or softmax work.  The mask must not change until the
+ *                queued work is done.
+ * Rows that see no key get o = 0 and lse = -inf and contribute nothing to any
+ * gradient.  N may be at most 524288 (4096 blocks); larger N returns
+ * FA_ERR_UNSUPPORTED.  Other arguments, validation and errors are those of
+ * fa_fwd / fa_bwd; fa_bwd_sparse needs o and lse from fa_fwd_sparse with the
+ * same mask.
+ */
+#define FA_SPARSE_BLOCK 128
+int fa_fwd_sparse(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int B, int H, int N, int d, const unsigned char *block_mask,
+                  float scale, int causal, fa_dtype dtype, void *stream);
+int fa_bwd_sparse(const void *q, const void *k, const void *v, const void *o,
+                  const void *dout, const float *lse,
+                  void *dq, void *dk, void *dv,
+                  void *workspace, size_t workspace_bytes,
+                  int B, int H, int N, int d, const unsigned char *block_mask,
+                  float scale, int causal, fa_dtype dtype, void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);

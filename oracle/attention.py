@@ -161,8 +161,8 @@ def attention_backward_rows(q, k, v, do, scale, causal, b, h, rows):
 # ---------------------------------------------------------------------------
 # Queries and keys of different counts, and padded batches.
 #
-# The pages apply causal masking "for autoregressive decoding" and apply
-# causal masking and padding per tile, with boundary tiles cut by the mask
+# The pages tie the causal mask to autoregressive decoding, and apply causal
+# masking and padding tile by tile, with boundary tiles cut by the mask
 # ("How Flash Attention Works: Tiling, Softmax, GPU I/O", sections "How Flash
 # Attention Works: The Exact-Attention Idea" and "Tiling Q, K, and V for Fast
 # On-Chip Memory").  They fix neither the alignment of a causal mask when the

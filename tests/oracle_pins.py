@@ -15,8 +15,8 @@ What each pin rests on:
     causal mask), causal row 0, N = 1, shift of every key by one vector;
   * invariants: probability rows sum to one, permutation equivariance;
   * the online recurrence: the running max / running normaliser update with
-    rescaling of the partial output "converges to the identical value"
-    as the full-row softmax ("How Flash Attention Works", section "Online
+    rescaling of the partial output ends at the same value as the full-row
+    softmax ("How Flash Attention Works", section "Online
     Softmax Without the Full Score Matrix"), written here independently;
   * library special cases: scipy.special.logsumexp for the LSE, and torch CPU
     float64 autograd of the naive expression for the outputs and gradients;

@@ -38,7 +38,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv",
-                                  "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_status_string", "fa_version"])
+                                  "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
+                                  "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -197,6 +198,48 @@ def test_bwd_kv_rejects(fa, name, kw, want):
     assert _bwd_kv(fa, **kw) == want
 
 
+# Block sparse: N = 256 -> a [1, 2, 2, 2] mask of 8 bytes.
+def _fwd_sp(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, N=256, d=64, m=_ptr(12),
+             scale=0.125, causal=1, dtype=fa.FA_F16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["m"],
+                            a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def _bwd_sp(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), dout=_ptr(4), lse=_ptr(5), dq=_ptr(6),
+             dk=_ptr(7), dv=_ptr(8), ws=_ptr(9), wsb=1 << 20, B=1, H=2, N=256, d=64, m=_ptr(12), scale=0.125,
+             causal=0, dtype=fa.FA_F16, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_sparse(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                            a["ws"], a["wsb"], a["B"], a["H"], a["N"], a["d"], a["m"], a["scale"], a["causal"],
+                            a["dtype"], a["stream"])
+
+
+SP_FWD_BAD = [
+    ("null mask", dict(m=None), -1), ("N=0", dict(N=0), -1), ("d=80", dict(d=80), -2),
+    ("N past the mask table", dict(N=524288 + 1), -2),
+    ("o over mask", dict(o=_ptr(12, -4096)), -1), ("lse over mask end", dict(lse=_ptr(12, 4)), -1),
+    ("null k", dict(k=None), -1), ("inf scale", dict(scale=float("inf")), -1),
+]
+SP_BWD_BAD = [
+    ("null mask", dict(m=None), -1), ("dk over mask", dict(dk=_ptr(12)), -1),
+    ("workspace over mask", dict(ws=_ptr(12, -16)), -3), ("small workspace", dict(wsb=8), -3),
+    ("misaligned dv", dict(dv=_ptr(8, 2)), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", SP_FWD_BAD, ids=[x[0] for x in SP_FWD_BAD])
+def test_fwd_sparse_rejects(fa, name, kw, want):
+    assert _fwd_sp(fa, **kw) == want
+
+
+@pytest.mark.parametrize("name,kw,want", SP_BWD_BAD, ids=[x[0] for x in SP_BWD_BAD])
+def test_bwd_sparse_rejects(fa, name, kw, want):
+    assert _bwd_sp(fa, **kw) == want
+
+
 @pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
 def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd(fa) == fa.FA_ERR_HIP
@@ -206,6 +249,8 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd_kv(fa) == fa.FA_ERR_HIP
     assert _fwd_kv(fa, sq=None, sk=None, Nq=1) == fa.FA_ERR_HIP
     assert _bwd_kv(fa) == fa.FA_ERR_HIP
+    assert _fwd_sp(fa) == fa.FA_ERR_HIP
+    assert _bwd_sp(fa) == fa.FA_ERR_HIP
 
 
 def test_python_helpers_refuse_cpu_tensors(fa):
