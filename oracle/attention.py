@@ -307,3 +307,95 @@ def attention_backward_sparse(q, k, v, do, scale, causal, block_mask, block=128)
             dq[b, h] = scale * (dsm @ k[b, h])
             dk[b, h] = scale * (dsm.T @ q[b, h])
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Dropout on the attention weights.  The pages list dropout among the work the
+# fused kernel does ("How Flash Attention Works", section "Kernel Fusion and
+# Incremental Output Accumulation") without a random-number scheme; the
+# reading taken here:
+#   * O = (P * Z) V with Z_ij = keep_ij / (1 - p); P is the softmax of the
+#     scores (its normaliser and the LSE do not see the dropout);
+#   * keep_ij = [r_ij >= floor(p * 2^32)] for a 32-bit word r_ij of the
+#     counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+#     "Parallel random numbers: as easy as 1, 2, 3", SC 2011): key = the 64-bit
+#     seed (low word first), counter = (j >> 2, i, b * H + h, offset), and
+#     r_ij is output word j & 3;
+#   * the backward is the chain rule through Z: dV = (P * Z)^T dO,
+#     dP = (dO V^T) * Z, D_i = sum_j P_ij dP_ij (= sum_c dO_ic O_ic),
+#     dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+# ---------------------------------------------------------------------------
+
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)  # round multipliers
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)  # key increments (golden ratio, sqrt(3) - 1)
+
+
+def philox4x32(c0, c1, c2, c3, k0, k1, rounds=10):
+    """Philox4x32-R on arrays of uint32 counters with a uint32 key pair; returns four uint32 arrays.
+
+    One round: (hi0, lo0) = M0 * c0, (hi1, lo1) = M1 * c2 (64-bit products);
+    c <- (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key gains (W0, W1)
+    between rounds.
+    """
+    m = np.uint64(0xFFFFFFFF)
+    c = [np.asarray(x, dtype=np.uint64) & m for x in (c0, c1, c2, c3)]
+    k0, k1 = np.uint64(k0) & m, np.uint64(k1) & m
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + np.uint64(_PHILOX_W[0])) & m
+            k1 = (k1 + np.uint64(_PHILOX_W[1])) & m
+        p0 = np.uint64(_PHILOX_M[0]) * c[0]
+        p1 = np.uint64(_PHILOX_M[1]) * c[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & m
+        hi1, lo1 = p1 >> np.uint64(32), p1 & m
+        c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+    return tuple(x.astype(np.uint32) for x in c)
+
+
+def dropout_threshold(p):
+    """keep iff the 32-bit word is >= this (p in [0, 1))."""
+    return int(np.floor(float(p) * 4294967296.0))
+
+
+def dropout_keep(n_q, n_k, bh, p, seed, offset):
+    """Boolean [n_q, n_k] keep mask of one (b, h) slice."""
+    i = np.arange(n_q, dtype=np.uint64)[:, None] * np.ones((1, n_k), dtype=np.uint64)
+    j = np.ones((n_q, 1), dtype=np.uint64) * np.arange(n_k, dtype=np.uint64)[None, :]
+    seed = int(seed)
+    words = philox4x32(j >> np.uint64(2), i, np.full(i.shape, bh, dtype=np.uint64),
+                       np.full(i.shape, int(offset) & 0xFFFFFFFF, dtype=np.uint64),
+                       seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    sel = (j & np.uint64(3)).astype(np.int64)
+    r = np.choose(sel, words)
+    return r >= np.uint32(dropout_threshold(p))
+
+
+def attention_forward_dropout(q, k, v, scale, causal, p, seed, offset):
+    """O = (P * Z) V and the (undropped) LSE for [B, H, N, d] inputs."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, _ = q.shape
+    o = np.empty(q.shape[:3] + (v.shape[3],))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            pr, lse[b, h] = _softmax_rows_kv(_scores_kv(q[b, h], k[b, h], scale, causal, 0))
+            z = dropout_keep(N, N, b * H + h, p, seed, offset) / (1.0 - p)
+            o[b, h] = (pr * z) @ v[b, h]
+    return o, lse
+
+
+def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
+    """dQ, dK, dV of L = sum(dO * O) for the dropout forward above."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, _ = q.shape
+    dq, dk, dv = np.empty(q.shape), np.empty(k.shape), np.empty(v.shape)
+    for b in range(B):
+        for h in range(H):
+            pr, _ = _softmax_rows_kv(_scores_kv(q[b, h], k[b, h], scale, causal, 0))
+            z = dropout_keep(N, N, b * H + h, p, seed, offset) / (1.0 - p)
+            dv[b, h] = (pr * z).T @ do[b, h]
+            dpz = (do[b, h] @ v[b, h].T) * z
+            dsz = pr * (dpz - np.sum(pr * dpz, axis=1, keepdims=True))
+            dq[b, h] = scale * (dsz @ k[b, h])
+            dk[b, h] = scale * (dsz.T @ q[b, h])
+    return dq, dk, dv

@@ -596,6 +596,134 @@ def pin_sparse_finite_differences(orc):
             assert err < 1e-7, f"sparse finite differences grad {which} causal={causal}: {err:.2e}"
 
 
+# ------------------------------------------------------------------ dropout
+# Reading (the pages name dropout as fused, with no generator): O = (P * Z) V,
+# Z = keep / (1 - p), keep_ij = [r_ij >= floor(p 2^32)], r_ij = word j & 3 of
+# Philox4x32-10 with key = seed and counter (j >> 2, i, b H + h, offset).
+def pin_philox_known_answers(orc):
+    with open(os.path.join(GOLDEN, "philox_kat.json")) as f:
+        g = json.load(f)
+    for vec in g["vectors"]:
+        ctr = [int(x, 16) for x in vec["counter"]]
+        key = [int(x, 16) for x in vec["key"]]
+        got = orc.philox4x32(*ctr, *key)
+        assert [int(x) for x in got] == [int(x, 16) for x in vec["output"]], f"Philox KAT {vec['counter']}"
+
+
+def _philox_scalar(c, k):
+    """Philox4x32-10 on Python ints, written out separately from the oracle's array version."""
+    c, k = list(c), list(k)
+    for r in range(10):
+        if r:
+            k = [(k[0] + 0x9E3779B9) & 0xFFFFFFFF, (k[1] + 0xBB67AE85) & 0xFFFFFFFF]
+        a, b = 0xD2511F53 * c[0], 0xCD9E8D57 * c[2]
+        c = [(b >> 32) ^ c[1] ^ k[0], b & 0xFFFFFFFF, (a >> 32) ^ c[3] ^ k[1], a & 0xFFFFFFFF]
+    return c
+
+
+def pin_dropout_p0_is_dense(orc):
+    q, k, v = _qkv(70, 2, 2, 17, 8)
+    do = _rng(71).standard_normal(q.shape)
+    for causal in (False, True):
+        o, lse = orc.attention_forward(q, k, v, 0.3, causal)
+        o2, lse2 = orc.attention_forward_dropout(q, k, v, 0.3, causal, 0.0, 1234, 5)
+        _close(o2, o, 1e-13, f"dropout p=0 O causal={causal}")
+        _close(lse2, lse, 1e-13, f"dropout p=0 LSE causal={causal}")
+        for a, b, n in zip(orc.attention_backward_dropout(q, k, v, do, 0.3, causal, 0.0, 1234, 5),
+                           orc.attention_backward(q, k, v, do, 0.3, causal), "QKV"):
+            _close(a, b, 1e-12, f"dropout p=0 d{n} causal={causal}")
+
+
+def pin_dropout_bruteforce(orc):
+    """Scalar loops: Philox on ints, the keep test, softmax, (P * Z) V."""
+    B, H, N, d = 1, 2, 9, 3
+    q, k, v = _qkv(72, B, H, N, d)
+    p, seed, offset = 0.35, 0xDEADBEEF12345, 7
+    t = math.floor(p * 2 ** 32)
+    for causal in (False, True):
+        o, lse = orc.attention_forward_dropout(q, k, v, 0.5, causal, p, seed, offset)
+        for h in range(H):
+            for i in range(N):
+                js = [j for j in range(N) if not causal or j <= i]
+                s = {j: 0.5 * math.fsum(x * y for x, y in zip(q[0, h, i], k[0, h, j])) for j in js}
+                mx = max(s.values())
+                w = {j: math.exp(s[j] - mx) for j in js}
+                z = math.fsum(w.values())
+                _close(lse[0, h, i], mx + math.log(z), 1e-12, "dropout LSE is the undropped one")
+                keep = {j: _philox_scalar((j >> 2, i, h, offset), (seed & 0xFFFFFFFF, seed >> 32))[j & 3] >= t
+                        for j in js}
+                for c in range(d):
+                    want = math.fsum(w[j] * v[0, h, j, c] for j in js if keep[j]) / z / (1 - p)
+                    _close(o[0, h, i, c], want, 1e-12, f"dropout brute O h={h} i={i} causal={causal}")
+
+
+def pin_dropout_keep_rate(orc):
+    """keep is Bernoulli(1 - p) per entry; streams differ across heads and offsets, repeat for the same ones."""
+    for p in (0.1, 0.5, 0.9):
+        m = orc.dropout_keep(256, 256, 3, p, 99, 0)
+        n = m.size
+        want = 1.0 - orc.dropout_threshold(p) / 2 ** 32
+        sd = math.sqrt(n * want * (1 - want))
+        assert abs(m.sum() - n * want) < 5 * sd, f"keep rate for p={p}: {m.mean():.4f} vs {want:.4f}"
+    a = orc.dropout_keep(64, 64, 3, 0.5, 99, 0)
+    assert np.array_equal(a, orc.dropout_keep(64, 64, 3, 0.5, 99, 0)), "same stream, same mask"
+    for other in (orc.dropout_keep(64, 64, 4, 0.5, 99, 0), orc.dropout_keep(64, 64, 3, 0.5, 99, 1),
+                  orc.dropout_keep(64, 64, 3, 0.5, 100, 0)):
+        assert 0.3 < np.mean(a != other) < 0.7, "independent streams for another head / offset / seed"
+
+
+def pin_dropout_unbiased(orc):
+    """E over seeds of O with dropout is the dense O (mean of 400 draws within 6 standard errors)."""
+    q, k, v = _qkv(73, 1, 1, 6, 4)
+    o_dense, _ = orc.attention_forward(q, k, v, 0.5, False)
+    draws = np.stack([orc.attention_forward_dropout(q, k, v, 0.5, False, 0.3, s, 0)[0] for s in range(400)])
+    mean, se = draws.mean(axis=0), draws.std(axis=0) / math.sqrt(len(draws))
+    assert np.all(np.abs(mean - o_dense) <= 6 * se + 1e-12), "dropout output is unbiased"
+
+
+def pin_dropout_torch_autograd(orc):
+    import torch
+    q, k, v = _qkv(74, 2, 2, 11, 5)
+    do = _rng(75).standard_normal(q.shape)
+    p, seed, offset = 0.25, 42, 3
+    z = np.stack([np.stack([orc.dropout_keep(11, 11, b * 2 + h, p, seed, offset) for h in range(2)])
+                  for b in range(2)]) / (1 - p)
+    for causal in (False, True):
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        s = 0.4 * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+        if causal:
+            s = s.masked_fill(torch.ones(11, 11, dtype=torch.bool).triu(1), float("-inf"))
+        out = torch.matmul(torch.softmax(s, dim=-1) * torch.tensor(z), tv)
+        (out * torch.tensor(do)).sum().backward()
+        o, _ = orc.attention_forward_dropout(q, k, v, 0.4, causal, p, seed, offset)
+        _close(o, out.detach().numpy(), 1e-12, f"dropout autograd O causal={causal}")
+        dq, dk, dv = orc.attention_backward_dropout(q, k, v, do, 0.4, causal, p, seed, offset)
+        _close(dq, tq.grad.numpy(), 1e-10, f"dropout autograd dQ causal={causal}")
+        _close(dk, tk.grad.numpy(), 1e-10, f"dropout autograd dK causal={causal}")
+        _close(dv, tv.grad.numpy(), 1e-10, f"dropout autograd dV causal={causal}")
+
+
+def pin_dropout_finite_differences(orc):
+    q, k, v = _qkv(76, 1, 1, 6, 3)
+    do = _rng(77).standard_normal(q.shape)
+    for causal in (False, True):
+        grads = orc.attention_backward_dropout(q, k, v, do, 0.45, causal, 0.3, 11, 2)
+        base = [q, k, v]
+        h = 1e-6
+        for which in range(3):
+            num = np.zeros_like(base[which])
+            for idx in np.ndindex(base[which].shape):
+                loss = []
+                for sgn in (1.0, -1.0):
+                    xs = [x.copy() for x in base]
+                    xs[which][idx] += sgn * h
+                    o, _ = orc.attention_forward_dropout(*xs, 0.45, causal, 0.3, 11, 2)
+                    loss.append(np.sum(o * do))
+                num[idx] = (loss[0] - loss[1]) / (2 * h)
+            err = np.max(np.abs(num - grads[which])) / max(1.0, np.max(np.abs(num)))
+            assert err < 1e-7, f"dropout finite differences grad {which} causal={causal}: {err:.2e}"
+
+
 ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pin_constant_v,
             pin_q_zero, pin_causal_row0_and_n1, pin_shift_invariance, pin_permutation,
             pin_online_recurrence, pin_scipy_logsumexp, pin_torch_autograd,
@@ -603,4 +731,6 @@ ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pi
             pin_kv_reduces_to_square, pin_kv_worked_example, pin_kv_bruteforce, pin_kv_decode_and_empty,
             pin_kv_padding_invariance, pin_kv_torch_autograd, pin_kv_finite_differences,
             pin_sparse_all_ones_is_dense, pin_sparse_bruteforce, pin_sparse_block_diagonal,
-            pin_sparse_torch_autograd, pin_sparse_finite_differences]
+            pin_sparse_torch_autograd, pin_sparse_finite_differences,
+            pin_philox_known_answers, pin_dropout_p0_is_dense, pin_dropout_bruteforce, pin_dropout_keep_rate,
+            pin_dropout_unbiased, pin_dropout_torch_autograd, pin_dropout_finite_differences]

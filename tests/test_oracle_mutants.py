@@ -48,6 +48,14 @@ MUTANTS = {
     "sparse mask ignored in backward": ("            s = np.where(_block_visible(bm[b, h], N, block), s, -np.inf)\n            p, _ = ",
                                         "            p, _ = "),
     "sparse dV not transposed": ("dv[b, h] = p.T @ do[b, h]", "dv[b, h] = p @ do[b, h]"),
+    "philox multiplier": ("_PHILOX_M = (0xD2511F53, 0xCD9E8D57)", "_PHILOX_M = (0xD2511F53, 0xCD9E8D55)"),
+    "philox key bump on every round": ("        if r:\n            k0 = (k0", "        if True:\n            k0 = (k0"),
+    "dropout keep below threshold": ("return r >= np.uint32(dropout_threshold(p))", "return r < np.uint32(dropout_threshold(p))"),
+    "dropout scaled by (1 - p)": ("z = dropout_keep(N, N, b * H + h, p, seed, offset) / (1.0 - p)\n            o[b, h]",
+                                  "z = dropout_keep(N, N, b * H + h, p, seed, offset) * (1.0 - p)\n            o[b, h]"),
+    "dropout counter transposed": ("words = philox4x32(j >> np.uint64(2), i,", "words = philox4x32(i >> np.uint64(2), j,"),
+    "dropout dP without Z": ("dpz = (do[b, h] @ v[b, h].T) * z", "dpz = (do[b, h] @ v[b, h].T)"),
+    "dropout dV without Z": ("dv[b, h] = (pr * z).T @ do[b, h]", "dv[b, h] = pr.T @ do[b, h]"),
     "kv dropped D term": ("ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))\n            dq[b, h, :a]",
                           "ds = p * dp\n            dq[b, h, :a]"),
 }
