@@ -1,10 +1,11 @@
 """Python binding of libfa, the gfx950 fused exact-attention library.
 
 The functions named like the C entry points (fa_fwd, fa_bwd, fa_fwd_kv,
-fa_bwd_kv, fa_fwd_sparse, fa_bwd_sparse, fa_bwd_workspace_bytes, ...) take raw
-device addresses and sizes exactly as include/fa.h declares them.  forward(),
-backward(), forward_kv(), backward_kv(), forward_sparse() and
-backward_sparse() are conveniences for torch tensors:
+fa_bwd_kv, fa_fwd_sparse, fa_bwd_sparse, fa_fwd_dropout, fa_bwd_dropout,
+fa_bwd_workspace_bytes, ...) take raw device addresses and sizes exactly as
+include/fa.h declares them.  forward(), backward(), forward_kv(),
+backward_kv(), forward_sparse(), backward_sparse(), forward_dropout() and
+backward_dropout() are conveniences for torch tensors:
 they check shapes, allocate the outputs with torch, pass data_ptr()s and
 torch's current HIP stream, and raise FaError on a non-zero status.  All
 arithmetic happens in the HIP kernels; there is no CPU or PyTorch fallback,
@@ -19,7 +20,8 @@ import os
 __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
            "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
-           "backward_kv", "forward_sparse", "backward_sparse", "SPARSE_BLOCK", "library_path", "load"]
+           "backward_kv", "forward_sparse", "backward_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
+           "forward_dropout", "backward_dropout", "SPARSE_BLOCK", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 SPARSE_BLOCK = 128  # rows and keys per block of a block-sparse mask (FA_SPARSE_BLOCK)
@@ -29,7 +31,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
-           "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_status_string", "fa_version")
+           "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
+           "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -53,6 +56,7 @@ def load() -> ctypes.CDLL:
                            "(there is no fallback implementation)")
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
@@ -71,6 +75,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_sparse.restype = i
     lib.fa_bwd_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, vp, f, i, i, vp]
     lib.fa_bwd_sparse.restype = i
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, u64, u32, i, vp]
+    lib.fa_fwd_dropout.restype = i
+    lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, f, u64, u32, i, vp]
+    lib.fa_bwd_dropout.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -126,6 +134,17 @@ def fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
                   scale, causal, dtype, stream) -> int:
     return load().fa_bwd_sparse(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                                 block_mask, scale, causal, dtype, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, offset, dtype, stream) -> int:
+    return load().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, causal, dropout_p, seed, offset, dtype,
+                                 stream)
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, causal,
+                   dropout_p, seed, offset, dtype, stream) -> int:
+    return load().fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
+                                 scale, causal, dropout_p, seed, offset, dtype, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
@@ -317,4 +336,39 @@ def backward_sparse(q, k, v, o, lse, dout, block_mask, scale=None, causal=False,
                        B, H, N, d, m.data_ptr(), scale, int(bool(causal)), code, _stream(q, stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_sparse")
+    return dq, dk, dv
+
+
+def forward_dropout(q, k, v, dropout_p, seed, offset=0, scale=None, causal=False, need_lse=True, stream=None):
+    """fa_fwd_dropout on torch tensors: O = (P o Z) v with a Philox keep mask drawn from (seed, offset)."""
+    import torch
+    _check(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if need_lse else None
+    st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr() if lse is not None else None, B, H, N, d, scale, int(bool(causal)),
+                        float(dropout_p), int(seed), int(offset), _dtype_code(q), _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_dropout")
+    return o, lse
+
+
+def backward_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, scale=None, causal=False, stream=None):
+    """fa_bwd_dropout on torch tensors (o and lse from forward_dropout with the same mask arguments)."""
+    import torch
+    _check(q, k, v, o, dout)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = fa_bwd_workspace_bytes(B, H, N, d, code)
+    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                        B, H, N, d, scale, int(bool(causal)), float(dropout_p), int(seed), int(offset), code,
+                        _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_dropout")
     return dq, dk, dv

@@ -54,11 +54,30 @@ size_t mask_bytes(int B, int H, int Nq, int Nk) {
   return (size_t)B * H * bq * bk;
 }
 
+// Dropout settings of one call (on = 0: none).  A weight is kept when its
+// 32-bit Philox word is >= threshold = floor(p * 2^32), so it is dropped with
+// probability threshold / 2^32 (p up to 2^-32); kept weights are scaled by
+// 1 / (1 - p).
+struct DropSpec {
+  int on;
+  unsigned threshold, seed_lo, seed_hi, offset;
+  float scale;
+};
+constexpr DropSpec kNoDrop{0, 0u, 0u, 0u, 0u, 1.0f};
+
+int drop_spec(float p, unsigned long long seed, unsigned offset, DropSpec* out) {
+  if (!(p >= 0.0f && p < 1.0f)) return FA_ERR_INVALID_ARG;  // also rejects NaN
+  const double t = std::floor((double)p * 4294967296.0);    // < 2^32 since p < 1
+  *out = DropSpec{p > 0.0f ? 1 : 0, (unsigned)t, (unsigned)(seed & 0xFFFFFFFFull), (unsigned)(seed >> 32), offset,
+                  (float)(1.0 / (1.0 - (double)p))};
+  return FA_OK;
+}
+
 // Forward validation and launch for q/o of Nq rows and k/v of Nk rows per
 // (batch, head), with optional device arrays of per-sequence lengths.
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
             const int* seqlens_q, const int* seqlens_k, const unsigned char* block_mask, float scale, int causal,
-            int dtype, void* stream) {
+            int dtype, void* stream, const DropSpec& drop = kNoDrop) {
   int st = check_shape(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
@@ -82,6 +101,8 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk; p.d = d;
   p.seqlens_q = seqlens_q; p.seqlens_k = seqlens_k;
   p.block_mask = block_mask;
+  p.drop_on = drop.on; p.drop_threshold = drop.threshold; p.drop_seed_lo = drop.seed_lo;
+  p.drop_seed_hi = drop.seed_hi; p.drop_offset = drop.offset; p.drop_scale = drop.scale;
   p.scale = scale; p.causal = causal; p.dtype = dtype;
   (void)hipGetLastError();  // report only this launch's error
   return hip_status(fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream)));
@@ -119,6 +140,15 @@ int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* l
   if (!block_mask) return FA_ERR_INVALID_ARG;
   if (N > kMaxSparseN) return FA_ERR_UNSUPPORTED;
   return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype, stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float dropout_p, unsigned long long seed, unsigned offset, fa_dtype dtype,
+                   void* stream) {
+  DropSpec drop;
+  int st = drop_spec(dropout_p, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, stream, drop);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
@@ -175,7 +205,7 @@ int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int Nq, in
 
 fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d, const int* seqlens_q,
                           const int* seqlens_k, const unsigned char* block_mask, float scale, int causal,
-                          int dtype) {
+                          int dtype, const DropSpec& drop = kNoDrop) {
   fa::BwdProblem b;
   auto use = [](const void* x) { return x == kUnused ? nullptr : x; };
   b.q = use(p.q); b.k = use(p.k); b.v = use(p.v); b.o = use(p.o); b.dout = use(p.dout);
@@ -185,6 +215,8 @@ fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d
   b.B = B; b.H = H; b.Nq = Nq; b.Nk = Nk; b.d = d;
   b.seqlens_q = seqlens_q; b.seqlens_k = seqlens_k;
   b.block_mask = block_mask;
+  b.drop_on = drop.on; b.drop_threshold = drop.threshold; b.drop_seed_lo = drop.seed_lo;
+  b.drop_seed_hi = drop.seed_hi; b.drop_offset = drop.offset; b.drop_scale = drop.scale;
   b.scale = scale; b.causal = causal; b.dtype = dtype;
   return b;
 }
@@ -229,6 +261,20 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
   int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
   return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype), 0, 2,
+                    stream);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, float dropout_p, unsigned long long seed, unsigned offset, fa_dtype dtype,
+                   void* stream) {
+  DropSpec drop;
+  int st = drop_spec(dropout_p, seed, offset, &drop);
+  if (st != FA_OK) return st;
+  const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, drop), 0, 2,
                     stream);
 }
 

@@ -38,6 +38,7 @@ struct BwdArgs {
   const int* seqlens_k;
   const unsigned char* block_mask;  // block-sparse: [B, H, nbq, nbk] (SPARSE kernels only)
   int nbq, nbk;
+  Dropout drop;                     // DROP kernels only
   int Nq, Nk, H;
   int nblk;    // blocks per head along the owned dimension
   int total;   // workgroups in the grid
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ o, c
   constexpr int EPL = 16 / sizeof(T);  // elements per lane (one 16-byte chunk)
   constexpr int LPR = D / EPL;         // lanes per row
   constexpr int RPB = 256 / LPR;       // rows per block
-  const int tid = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + tid / LPR;
+  const int tid = thread_id();
+  const long long row = (long long)block_id() * RPB + tid / LPR;
   const int part = tid % LPR;
   float acc = 0.0f;
   if (row < rows) {
@@ -89,7 +90,7 @@ struct BwdLayout {
 
 // --------------------------------------------------------------------------
 // dK, dV for 128 keys per workgroup.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using M = Mma<T>;
   using L = BwdLayout<T, D>;
@@ -104,12 +105,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   float* lds_lse = reinterpret_cast<float*>(lds_do + 2 * L::TILE);  // [2][64], log2 units
   float* lds_d = lds_lse + 2 * kBwdTile;                            // [2][64]
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bid = xcd_remap(block_id(), a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);  // wave-uniform: keep scalar
   const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   const int kb0 = kblk * kBwdOwn;
@@ -233,6 +234,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           const int rr = 32 * qb + 8 * g + 4 * h;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rr);
+          const uint32_t kbits = DROP ? a.drop.quad_keep(mykey >> 2, i0 + rr, bh, col & 3) : 0u;
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * g + u;
@@ -242,8 +244,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
               const bool ok = qi < sq.lq && (!CAUSAL || mykey <= qi + sq.off);
               p = ok ? p : 0.0f;
             }
-            s[r] = p;
-            dp[r] = p * (dp[r] - d4[u]);
+            if constexpr (DROP) {
+              // dV takes the kept weights (1 / (1 - p) at the store); dP of a
+              // dropped weight is 0, of a kept one dP / (1 - p)
+              const bool kp = (kbits >> (4 * u)) & 1u;
+              s[r] = kp ? p : 0.0f;
+              dp[r] = p * ((kp ? dp[r] * a.drop.scale : 0.0f) - d4[u]);
+            } else {
+              s[r] = p;
+              dp[r] = p * (dp[r] - d4[u]);
+            }
           }
         }
         // dV^T += dO^T P,  dK^T += Q^T dS   (contraction over this block's 32 queries)
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           k4[u] = real ? dkacc[mb][4 * g + u] * sc : 0.0f;
-          v4[u] = real ? dvacc[mb][4 * g + u] : 0.0f;
+          v4[u] = real ? dvacc[mb][4 * g + u] * (DROP ? a.drop.scale : 1.0f) : 0.0f;
         }
         store4<T>(dkrow + d0, k4[0], k4[1], k4[2], k4[3]);
         store4<T>(dvrow + d0, v4[0], v4[1], v4[2], v4[3]);
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // --------------------------------------------------------------------------
 // dQ for 128 queries per workgroup.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using M = Mma<T>;
   using L = BwdLayout<T, D>;
@@ -300,12 +310,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   T* lds_k = reinterpret_cast<T*>(smem);  // [2][TILE]
   T* lds_v = lds_k + 2 * L::TILE;          // [2][TILE]
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bid = xcd_remap(block_id(), a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);  // wave-uniform: keep scalar
   int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   if (CAUSAL) qb = a.nblk - 1 - qb;
@@ -402,6 +412,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
           dp = M::mma(row_frag<T>(vrow + ks * M::KS, h), dof[ks], dp);
         }
         // s^T: rows = keys k0 + 32 kb + acc_row(r, h), column = query myq
+        u32x4v w[4];  // dropout words of the four 4-key groups
+        if constexpr (DROP) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) w[g] = a.drop.words((k0 + 32 * kb + 8 * g + 4 * h) >> 2, myq, bh);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
@@ -409,7 +424,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
             const int key = k0 + 32 * kb + acc_row(r, h);
             p = key <= lim ? p : 0.0f;
           }
-          dp[r] = p * (dp[r] - dq_d);
+          if constexpr (DROP)
+            dp[r] = p * ((w[r >> 2][r & 3] >= a.drop.threshold ? dp[r] * a.drop.scale : 0.0f) - dq_d);
+          else
+            dp[r] = p * (dp[r] - dq_d);
         }
         // dQ^T += K^T dS^T  (contraction over this block's 32 keys)
 #pragma unroll
@@ -443,7 +461,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------------------
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t stream) {
   if (stage == 0) {
     const long long rows = (long long)p.B * p.H * p.Nq;
@@ -459,6 +477,7 @@ static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t strea
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.dvec = p.dvec;
   a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
   a.block_mask = p.block_mask;
+  a.drop = Dropout{p.drop_threshold, p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_scale};
   a.nbq = (p.Nq + kMaskBlock - 1) / kMaskBlock;
   a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
@@ -467,22 +486,26 @@ static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t strea
   a.nblk = ((stage == 1 ? p.Nk : p.Nq) + kBwdOwn - 1) / kBwdOwn;
   a.total = a.nblk * p.B * p.H;
   if (stage == 1)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(kBwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, bool SPARSE>
+template <typename T, bool SPARSE, bool DROP>
 static hipError_t launch_bwd_s(const BwdProblem& p, int stage, hipStream_t s) {
   if (p.d == 64)
-    return p.causal ? launch_bwd_t<T, 64, true, SPARSE>(p, stage, s) : launch_bwd_t<T, 64, false, SPARSE>(p, stage, s);
-  return p.causal ? launch_bwd_t<T, 128, true, SPARSE>(p, stage, s) : launch_bwd_t<T, 128, false, SPARSE>(p, stage, s);
+    return p.causal ? launch_bwd_t<T, 64, true, SPARSE, DROP>(p, stage, s)
+                    : launch_bwd_t<T, 64, false, SPARSE, DROP>(p, stage, s);
+  return p.causal ? launch_bwd_t<T, 128, true, SPARSE, DROP>(p, stage, s)
+                  : launch_bwd_t<T, 128, false, SPARSE, DROP>(p, stage, s);
 }
 
+// (block sparsity and dropout are not combined: the API rejects that)
 template <typename T>
 static hipError_t launch_bwd_d(const BwdProblem& p, int stage, hipStream_t s) {
-  return p.block_mask != nullptr ? launch_bwd_s<T, true>(p, stage, s) : launch_bwd_s<T, false>(p, stage, s);
+  if (p.drop_on) return launch_bwd_s<T, false, true>(p, stage, s);
+  return p.block_mask != nullptr ? launch_bwd_s<T, true, false>(p, stage, s) : launch_bwd_s<T, false, false>(p, stage, s);
 }
 
 #ifndef FA_DQ16

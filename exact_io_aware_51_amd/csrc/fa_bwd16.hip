@@ -33,6 +33,7 @@ struct Bwd16Args {
   const int* seqlens_k;
   const unsigned char* block_mask;  // block-sparse: [B, H, nbq, nbk] (SPARSE kernels only)
   int nbq, nbk;
+  Dropout drop;                     // DROP kernels only
   int Nq, Nk, H;
   int nblk;
   int total;
@@ -74,7 +75,7 @@ __device__ inline void reads_ahead() {
 #define FA_DQ_OCC128 1
 #endif
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(Bwd16Args a) {
   using M = Mma<T>;
   using TL = Tile16<D>;
@@ -86,13 +87,13 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
 
   __shared__ __attribute__((aligned(1024))) char smem[5 * TL::BYTES];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bid = xcd_remap(block_id(), a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
   int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   if (CAUSAL) qb = a.nblk - 1 - qb;
@@ -210,6 +211,12 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
 #endif
         if (kb == 0 && prev) dq_prev(kps);
         const int tk = t0 - 32 * kb;
+        // dropout: dP of a dropped weight is 0, of a kept one dP / (1 - p)
+        u32x4v w[4];
+        if constexpr (DROP) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) w[g] = a.drop.words((k0 + 32 * kb + 8 * g + 4 * h) >> 2, myq, bh);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float e = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
@@ -217,7 +224,10 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
             const int ro = 8 * (r >> 2) + (r & 3);
             e = ro <= tk ? e : 0.0f;
           }
-          p[r] = e * (p[r] - dd);
+          if constexpr (DROP)
+            p[r] = e * ((w[r >> 2][r & 3] >= a.drop.threshold ? p[r] * a.drop.scale : 0.0f) - dd);
+          else
+            p[r] = e * (p[r] - dd);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) dsf[kb][t] = acc_frag<T>(p, t);
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
 // The four accumulators (dK^T, dV^T) and the stationary fragments need about
 // 280 VGPRs, so one wave per SIMD runs this kernel; the element-wise work of
 // one half overlaps the matrix ops of the other inside the wave.
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
   using M = Mma<T>;
   using TL = Tile16<D>;
@@ -324,13 +334,13 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TL::BYTES + 1024];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bid = xcd_remap(block_id(), a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
   const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
   const int kb0 = kblk * 128;
@@ -448,6 +458,8 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
         const int rr = 32 * qb + 8 * g + 4 * h;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rr);
+        // dropout keep bits of queries i0 + rr .. + 3 against this lane's key
+        const uint32_t kbits = DROP ? a.drop.quad_keep(mykey >> 2, i0 + rr, bh, col & 3) : 0u;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * g + u;
@@ -456,8 +468,16 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
             const int qi = i0 + rr + u;
             p = (qi < sq.lq && (!CAUSAL || mykey <= qi + sq.off)) ? p : 0.0f;
           }
-          s[r] = p;
-          dp[r] = p * (dp[r] - d4[u]);
+          if constexpr (DROP) {
+            // dropout: dV takes the kept weights (1 / (1 - p) applied at the
+            // store); dP of a dropped weight is 0, of a kept one dP / (1 - p)
+            const bool kp = (kbits >> (4 * u)) & 1u;
+            s[r] = kp ? p : 0.0f;
+            dp[r] = p * ((kp ? dp[r] * a.drop.scale : 0.0f) - d4[u]);
+          } else {
+            s[r] = p;
+            dp[r] = p * (dp[r] - d4[u]);
+          }
         }
       }
 #pragma unroll
@@ -543,6 +563,7 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
     T* dvrow = reinterpret_cast<T*>(a.dv) + headk + (size_t)mykey * D;
     const bool real = mykey < sq.lk;
     const float sc = a.scale;
+    const float sv = DROP ? a.drop.scale : 1.0f;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -552,7 +573,7 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           k4[u] = real ? dkacc[mb][4 * g + u] * sc : 0.0f;
-          v4[u] = real ? dvacc[mb][4 * g + u] : 0.0f;
+          v4[u] = real ? dvacc[mb][4 * g + u] * sv : 0.0f;
         }
         store4<T>(dkrow + d0, k4[0], k4[1], k4[2], k4[3]);
         store4<T>(dvrow + d0, v4[0], v4[1], v4[2], v4[3]);
@@ -570,6 +591,7 @@ static Bwd16Args bwd16_args(const BwdProblem& p, int nblk) {
   a.block_mask = p.block_mask;
   a.nbq = (p.Nq + kMaskBlock - 1) / kMaskBlock;
   a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
+  a.drop = Dropout{p.drop_threshold, p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_scale};
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.scale = p.scale;
   a.c = p.scale * kLog2e;
@@ -579,43 +601,54 @@ static Bwd16Args bwd16_args(const BwdProblem& p, int nblk) {
 }
 static_assert(kMaskBlock == 128, "a dK/dV workgroup's 128 keys are one mask block column");
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
   const Bwd16Args a = bwd16_args(p, (p.Nk + 127) / 128);
-  hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, bool SPARSE>
+template <typename T, bool SPARSE, bool DROP>
 static hipError_t launch_dkdv16_s(const BwdProblem& p, hipStream_t s) {
   if (p.d == 64)
-    return p.causal ? launch_dkdv16_t<T, 64, true, SPARSE>(p, s) : launch_dkdv16_t<T, 64, false, SPARSE>(p, s);
-  return p.causal ? launch_dkdv16_t<T, 128, true, SPARSE>(p, s) : launch_dkdv16_t<T, 128, false, SPARSE>(p, s);
+    return p.causal ? launch_dkdv16_t<T, 64, true, SPARSE, DROP>(p, s) : launch_dkdv16_t<T, 64, false, SPARSE, DROP>(p, s);
+  return p.causal ? launch_dkdv16_t<T, 128, true, SPARSE, DROP>(p, s)
+                  : launch_dkdv16_t<T, 128, false, SPARSE, DROP>(p, s);
+}
+
+// (block sparsity and dropout are not combined: the API rejects that)
+template <typename T>
+static hipError_t launch_dkdv16_d(const BwdProblem& p, hipStream_t s) {
+  if (p.drop_on) return launch_dkdv16_s<T, false, true>(p, s);
+  return p.block_mask ? launch_dkdv16_s<T, true, false>(p, s) : launch_dkdv16_s<T, false, false>(p, s);
 }
 
 hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s) {
-  if (p.dtype == 1)
-    return p.block_mask ? launch_dkdv16_s<_Float16, true>(p, s) : launch_dkdv16_s<_Float16, false>(p, s);
-  return p.block_mask ? launch_dkdv16_s<__bf16, true>(p, s) : launch_dkdv16_s<__bf16, false>(p, s);
+  return p.dtype == 1 ? launch_dkdv16_d<_Float16>(p, s) : launch_dkdv16_d<__bf16>(p, s);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dq16_t(const BwdProblem& p, hipStream_t stream) {
   const Bwd16Args a = bwd16_args(p, (p.Nq + 127) / 128);
-  hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((dq16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, bool SPARSE>
+template <typename T, bool SPARSE, bool DROP>
 static hipError_t launch_dq16_s(const BwdProblem& p, hipStream_t s) {
   if (p.d == 64)
-    return p.causal ? launch_dq16_t<T, 64, true, SPARSE>(p, s) : launch_dq16_t<T, 64, false, SPARSE>(p, s);
-  return p.causal ? launch_dq16_t<T, 128, true, SPARSE>(p, s) : launch_dq16_t<T, 128, false, SPARSE>(p, s);
+    return p.causal ? launch_dq16_t<T, 64, true, SPARSE, DROP>(p, s) : launch_dq16_t<T, 64, false, SPARSE, DROP>(p, s);
+  return p.causal ? launch_dq16_t<T, 128, true, SPARSE, DROP>(p, s) : launch_dq16_t<T, 128, false, SPARSE, DROP>(p, s);
+}
+
+template <typename T>
+static hipError_t launch_dq16_d(const BwdProblem& p, hipStream_t s) {
+  if (p.drop_on) return launch_dq16_s<T, false, true>(p, s);
+  return p.block_mask ? launch_dq16_s<T, true, false>(p, s) : launch_dq16_s<T, false, false>(p, s);
 }
 
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s) {
-  if (p.dtype == 1) return p.block_mask ? launch_dq16_s<_Float16, true>(p, s) : launch_dq16_s<_Float16, false>(p, s);
-  return p.block_mask ? launch_dq16_s<__bf16, true>(p, s) : launch_dq16_s<__bf16, false>(p, s);
+  return p.dtype == 1 ? launch_dq16_d<_Float16>(p, s) : launch_dq16_d<__bf16>(p, s);
 }
 
 }  // namespace fa

@@ -170,6 +170,14 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Blocks are dispatched round-robin over the 8 XCDs (blockIdx % 8 = XCD).
 // Renumber them so that consecutive logical indices share an XCD (and so its
 // L2): XCD x receives logical blocks [x*q + min(x, r), ...) in order.
+// Work-item and work-group ids straight from the hardware registers.  The
+// kernels are built with IEEE mode off, which the device library is not, and
+// LLVM does not inline across that difference: threadIdx / blockIdx (and
+// __umulhi) would become real calls, turning every kernel into a non-leaf
+// function.
+__device__ __attribute__((always_inline)) inline int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __attribute__((always_inline)) inline int block_id() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+
 __device__ inline int xcd_remap(int bid, int total) {
   const int q = total >> 3, r = total & 7;
   const int x = bid & 7, local = bid >> 3;
@@ -200,6 +208,58 @@ __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t 
 
 // Wave-uniform "does any lane want this".
 __device__ inline bool any_lane(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
+
+// Counter-based random words: Philox4x32 with 10 rounds (Salmon, Moraes, Dror
+// and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).  One round
+// multiplies counter words 0 and 2 by the two round constants (64-bit
+// products), then c <- (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key gains
+// the two Weyl increments between rounds.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ inline u32x4v philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
+    c0 = hi1 ^ c1 ^ (k0 + r * W0);
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ (k1 + r * W1);
+    c3 = lo0;
+  }
+  return u32x4v{c0, c1, c2, c3};
+}
+
+// Dropout on the attention weights of one (batch, head): keep_ij when word
+// j & 3 of Philox(counter (j >> 2, i, bh, offset), key = seed) is at least the
+// threshold floor(p 2^32).  Kept weights are scaled by 1 / (1 - p) (`scale`),
+// which the kernels fold into their final normalisation.
+struct Dropout {
+  uint32_t threshold;
+  uint32_t seed_lo, seed_hi;
+  uint32_t offset;
+  float scale;
+  // the four random words of keys 4 g .. 4 g + 3 (g = j >> 2) for query i
+  __device__ inline u32x4v words(int g, int i, int bh) const {
+    return philox4x32_10((uint32_t)g, (uint32_t)i, (uint32_t)bh, offset, seed_lo, seed_hi);
+  }
+  // Keep bits for a lane that holds one key (4 g + c, c = lane & 3, the same g
+  // across its DPP quad of four lanes) against queries i0 .. i0 + 3.  Each lane
+  // draws the words of one query (i0 + c), which cover the quad's four keys;
+  // the four 4-bit keep rows are gathered across the quad, so one draw serves
+  // four weights instead of one.  Bit 4 u of the result keeps query i0 + u.
+  // Needs all four lanes of the quad active.
+  __device__ __attribute__((always_inline)) inline uint32_t quad_keep(int g, int i0, int bh, int c) const {
+    const u32x4v w = words(g, i0 + c, bh);
+    uint32_t m = (w[0] >= threshold ? 1u : 0u) | (w[1] >= threshold ? 2u : 0u) | (w[2] >= threshold ? 4u : 0u) |
+                 (w[3] >= threshold ? 8u : 0u);
+    m <<= 4 * c;                                                               // row c of the 4 x 4 keep block
+    m |= (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+    m |= (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
+    return m >> c;                                                             // column c: this lane's key
+  }
+};
 
 // Floor of a / b for b > 0 and any sign of a.
 __device__ inline int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }

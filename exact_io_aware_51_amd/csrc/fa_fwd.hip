@@ -35,6 +35,7 @@ struct FwdArgs {
   const int* seqlens_k;
   const unsigned char* block_mask;  // block-sparse: [B, H, nqb, nbk] (SPARSE kernels only)
   int nbk;
+  Dropout drop;                     // DROP kernels only
   int Nq, Nk, H;
   int nqb;     // query blocks per head
   int total;   // workgroups in the grid
@@ -88,7 +89,7 @@ __device__ inline void interleave() {
   __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) void fwd_kernel(FwdArgs a) {
   using M = Mma<T>;
   using L = FwdLayout<T, D>;
@@ -101,14 +102,14 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   T* lds_k = smem;                 // [2][KTILE]
   T* lds_v = smem + 2 * L::KTILE;  // [2][VTILE]
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
   // block coordinates are wave-uniform; keep them (and every address built
   // from them) in scalar registers
-  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bid = xcd_remap(block_id(), a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
   int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
   if (CAUSAL) qb = a.nqb - 1 - qb;  // the longest causal rows start first
@@ -235,6 +236,19 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
       s1[r] = p1;
       l += p0 + p1;
     }
+    // dropout: zero the weights of dropped keys (1 / (1 - p) goes with 1 / l)
+    if constexpr (DROP) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4v w0 = a.drop.words((k0 + 8 * g + 4 * h) >> 2, myq, bh);
+        const u32x4v w1 = a.drop.words((k0 + 32 + 8 * g + 4 * h) >> 2, myq, bh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s0[4 * g + u] = w0[u] >= a.drop.threshold ? s0[4 * g + u] : 0.0f;
+          s1[4 * g + u] = w1[u] >= a.drop.threshold ? s1[4 * g + u] : 0.0f;
+        }
+      }
+    }
     // O^T += V^T P^T over the tile's 64 keys
 #pragma unroll
     for (int t = 0; t < PSTEPS; ++t) {
@@ -292,7 +306,7 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   l = halves_sum(l);
   if (myq < Nq) {
     const bool real = myq < sq.lq && l > 0.0f;
-    const float inv = real ? 1.0f / l : 0.0f;
+    const float inv = real ? (DROP ? a.drop.scale : 1.0f) / l : 0.0f;
     T* orow = reinterpret_cast<T*>(a.o) + (size_t)bh * (size_t)Nq * D + (size_t)myq * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -309,7 +323,7 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   FwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
@@ -317,25 +331,29 @@ static hipError_t launch_fwd_t(const FwdProblem& p, hipStream_t stream) {
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.block_mask = p.block_mask;
   a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
+  a.drop = Dropout{p.drop_threshold, p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_scale};
   a.nqb = (p.Nq + kFwdBM - 1) / kFwdBM;
   static_assert(kFwdBM == kMaskBlock, "one workgroup's query rows are one mask block row");
   a.total = a.nqb * p.B * p.H;
   const float sc = p.scale;
   a.negate = sc < 0.0f;
   a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
-  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(kFwdThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, bool SPARSE>
+template <typename T, bool SPARSE, bool DROP>
 static hipError_t launch_fwd_s(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_fwd_t<T, 64, true, SPARSE>(p, s) : launch_fwd_t<T, 64, false, SPARSE>(p, s);
-  return p.causal ? launch_fwd_t<T, 128, true, SPARSE>(p, s) : launch_fwd_t<T, 128, false, SPARSE>(p, s);
+  if (p.d == 64)
+    return p.causal ? launch_fwd_t<T, 64, true, SPARSE, DROP>(p, s) : launch_fwd_t<T, 64, false, SPARSE, DROP>(p, s);
+  return p.causal ? launch_fwd_t<T, 128, true, SPARSE, DROP>(p, s) : launch_fwd_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
+// (block sparsity and dropout are not combined: the API rejects that)
 template <typename T>
 static hipError_t launch_fwd_d(const FwdProblem& p, hipStream_t s) {
-  return p.block_mask != nullptr ? launch_fwd_s<T, true>(p, s) : launch_fwd_s<T, false>(p, s);
+  if (p.drop_on) return launch_fwd_s<T, false, true>(p, s);
+  return p.block_mask != nullptr ? launch_fwd_s<T, true, false>(p, s) : launch_fwd_s<T, false, false>(p, s);
 }
 
 #ifndef FA_FWD16

@@ -45,6 +45,7 @@ struct Fwd16Args {
   const int* seqlens_k;
   const unsigned char* block_mask;  // block-sparse: [B, H, nqb, nbk] (SPARSE kernels only)
   int nbk;
+  Dropout drop;                     // DROP kernels only
   int Nq, Nk, H;
   int nqb;
   int total;
@@ -66,7 +67,7 @@ struct Fwd16Args {
 #define FA_FWD_BN64 64
 #endif
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   constexpr int BN = D == 64 ? FA_FWD_BN64 : 64;  // keys per tile
   constexpr int KB = BN / 32;                      // 32-key blocks per tile
@@ -80,13 +81,13 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 
   __shared__ __attribute__((aligned(1024))) char smem[4 * TL::BYTES];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(blockIdx.x, a.total);
+  const int bid = xcd_remap(block_id(), a.total);
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
   int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
   if (CAUSAL) qb = a.nqb - 1 - qb;
@@ -157,6 +158,24 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   float l = 0.0f;
   const float c = a.c;
 
+  // dropout: zero the weights of dropped keys in x (registers 8 t .. 8 t + 7
+  // of 32-key block kb, keys k0 + 32 kb + acc_row(r, h)); 1 / (1 - p) is
+  // applied with the final 1 / l
+  auto drop_mask = [&](f32x16& x, int kb, int t, int k0) __attribute__((always_inline)) {
+    if constexpr (DROP) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int j0 = k0 + 32 * kb + 8 * (2 * t + gg) + 4 * h;
+        const u32x4v w = a.drop.words(j0 >> 2, myq, bh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 8 * t + 4 * gg + u;
+          x[r] = w[u] >= a.drop.threshold ? x[r] : 0.0f;
+        }
+      }
+    }
+  };
+
   auto pv = [&](int vstage) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -224,6 +243,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
               p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, negm));
               rs += p8[8 * t + e];
             }
+            drop_mask(p8, kb, t, k0);
             pf[kb][t] = acc_frag<T>(p8, t);
           }
         if (any_lane(rs > 256.0f)) {
@@ -245,6 +265,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
                 p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, -mnew));
                 rs += p8[8 * t + e];
               }
+              drop_mask(p8, kb, t, k0);
               pf[kb][t] = acc_frag<T>(p8, t);
             }
 #pragma unroll
@@ -294,6 +315,10 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
           sc[kb][r] = p;
           rs += p;
         }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) drop_mask(sc[kb], kb, t, k0);
       if (need) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
@@ -389,7 +414,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   l = halves_sum(l);
   if (myq < Nq) {
     const bool real = myq < sq.lq && l > 0.0f;
-    const float inv = real ? 1.0f / l : 0.0f;
+    const float inv = real ? (DROP ? a.drop.scale : 1.0f) / l : 0.0f;
     T* orow = reinterpret_cast<T*>(a.o) + (size_t)bh * (size_t)Nq * D + (size_t)myq * D;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -406,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   Fwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
@@ -414,26 +439,29 @@ static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   a.Nq = p.Nq; a.Nk = p.Nk; a.H = p.H;
   a.block_mask = p.block_mask;
   a.nbk = (p.Nk + kMaskBlock - 1) / kMaskBlock;
+  a.drop = Dropout{p.drop_threshold, p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_scale};
   a.nqb = (p.Nq + 127) / 128;
   static_assert(kMaskBlock == 128, "one workgroup's 128 query rows are one mask block row");
   a.total = a.nqb * p.B * p.H;
   const float sc = p.scale;
   a.negate = sc < 0.0f;
   a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, SPARSE>), dim3(a.total), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, bool SPARSE>
+template <typename T, bool SPARSE, bool DROP>
 static hipError_t launch_fwd16_s(const FwdProblem& p, hipStream_t s) {
   if (p.d == 64)
-    return p.causal ? launch_fwd16_t<T, 64, true, SPARSE>(p, s) : launch_fwd16_t<T, 64, false, SPARSE>(p, s);
-  return p.causal ? launch_fwd16_t<T, 128, true, SPARSE>(p, s) : launch_fwd16_t<T, 128, false, SPARSE>(p, s);
+    return p.causal ? launch_fwd16_t<T, 64, true, SPARSE, DROP>(p, s) : launch_fwd16_t<T, 64, false, SPARSE, DROP>(p, s);
+  return p.causal ? launch_fwd16_t<T, 128, true, SPARSE, DROP>(p, s) : launch_fwd16_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
+// (block sparsity and dropout are not combined: the API rejects that)
 template <typename T>
 static hipError_t launch_fwd16_d(const FwdProblem& p, hipStream_t s) {
-  return p.block_mask != nullptr ? launch_fwd16_s<T, true>(p, s) : launch_fwd16_s<T, false>(p, s);
+  if (p.drop_on) return launch_fwd16_s<T, false, true>(p, s);
+  return p.block_mask != nullptr ? launch_fwd16_s<T, true, false>(p, s) : launch_fwd16_s<T, false, false>(p, s);
 }
 
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s) {

@@ -22,6 +22,11 @@ struct FwdProblem {
   // optional device uint8 [B, H, ceil(Nq/128), ceil(Nk/128)]: 0 removes the
   // scores of that (128-query block, 128-key block) pair (nullptr: dense)
   const unsigned char* block_mask;
+  // dropout on the attention weights (drop_on = 0: none): keep when Philox
+  // word >= drop_threshold, kept weights scaled by drop_scale = 1 / (1 - p)
+  int drop_on;
+  unsigned drop_threshold, drop_seed_lo, drop_seed_hi, drop_offset;
+  float drop_scale;
   float scale;
   int causal;
   int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
@@ -42,6 +47,9 @@ struct BwdProblem {
   const int* seqlens_q;
   const int* seqlens_k;
   const unsigned char* block_mask;  // as in FwdProblem
+  int drop_on;                      // as in FwdProblem
+  unsigned drop_threshold, drop_seed_lo, drop_seed_hi, drop_offset;
+  float drop_scale;
   float scale;
   int causal;
   int dtype;

@@ -188,6 +188,43 @@ int fa_bwd_sparse(const void *q, const void *k, const void *v, const void *o,
                   int B, int H, int N, int d, const unsigned char *block_mask,
                   float scale, int causal, fa_dtype dtype, void *stream);
 
+/*
+ * Attention dropout inside the fused kernel.  The pages count dropout among
+ * the steps an unfused pipeline runs as separate kernels and put it inside the
+ * one fused kernel ("How Flash Attention Works", sections "Why Standard
+ * Attention Becomes a GPU Memory I/O Bottleneck" and "Kernel Fusion and
+ * Incremental Output Accumulation"); they fix no random number generator and
+ * no mask layout.  These entry points take:
+ *   O = (P o Z) V with P = softmax(scale * q k^T [+ causal]) and
+ *   Z_ij = keep_ij / (1 - dropout_p).  lse is that of P (before dropout), so
+ *   fa_bwd_dropout recomputes P exactly as fa_bwd does.
+ *   keep_ij: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
+ *   Numbers: As Easy as 1, 2, 3", SC 2011) with key (seed mod 2^32,
+ *   seed >> 32) and counter (j >> 2, i, b * H + h, offset) yields four 32-bit
+ *   words; word (j & 3) decides key j of query row i, kept iff
+ *   word >= floor(dropout_p * 2^32).  Nothing is stored: the backward pass
+ *   regenerates the same words.  Calls with the same (seed, offset) draw the
+ *   same mask; advance offset (or change seed) for a fresh one.
+ *   dropout_p : in [0, 1), else FA_ERR_INVALID_ARG (NaN included).  0 runs
+ *               the fa_fwd / fa_bwd kernels and gives their results.
+ * Other arguments, validation and errors are those of fa_fwd / fa_bwd;
+ * fa_bwd_dropout needs o and lse from fa_fwd_dropout with the same arguments,
+ * and computes the gradients of sum(dout * O) for that fixed mask:
+ *   dV = (P o Z)^T dO,  dS = P o (Z o (dO V^T) - D),  D_i = sum_c dO_ic O_ic,
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ */
+int fa_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, unsigned int offset,
+                   fa_dtype dtype, void *stream);
+int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse,
+                   void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float dropout_p, unsigned long long seed, unsigned int offset,
+                   fa_dtype dtype, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -10,6 +10,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -39,7 +40,7 @@ def _declared():
 def test_header_declares_the_abi():
     assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv",
                                   "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
-                                  "fa_status_string", "fa_version"])
+                                  "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_string", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -240,6 +241,46 @@ def test_bwd_sparse_rejects(fa, name, kw, want):
     assert _bwd_sp(fa, **kw) == want
 
 
+# Dropout: the probability must lie in [0, 1); seed and offset take any value.
+def _fwd_dp(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, N=256, d=64, scale=0.125,
+             causal=1, p=0.1, seed=(1 << 64) - 1, offset=(1 << 32) - 1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                             a["scale"], a["causal"], a["p"], a["seed"], a["offset"], a["dtype"], a["stream"])
+
+
+def _bwd_dp(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), dout=_ptr(4), lse=_ptr(5), dq=_ptr(6),
+             dk=_ptr(7), dv=_ptr(8), ws=_ptr(9), wsb=1 << 20, B=1, H=2, N=256, d=64, scale=0.125,
+             causal=0, p=0.25, seed=7, offset=3, dtype=fa.FA_F16, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_dropout(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                             a["ws"], a["wsb"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["p"],
+                             a["seed"], a["offset"], a["dtype"], a["stream"])
+
+
+DP_FWD_BAD = [
+    ("p=1", dict(p=1.0), -1), ("p<0", dict(p=-1e-3), -1), ("p=nan", dict(p=float("nan")), -1),
+    ("p=inf", dict(p=float("inf")), -1), ("N=0", dict(N=0), -1), ("d=96", dict(d=96), -2),
+    ("null v", dict(v=None), -1), ("o over q", dict(o=_ptr(0, 16)), -1), ("dtype 7", dict(dtype=7), -2),
+]
+DP_BWD_BAD = [
+    ("p=1", dict(p=1.0), -1), ("p=nan", dict(p=float("nan")), -1), ("null lse", dict(lse=None), -1),
+    ("small workspace", dict(wsb=8), -3), ("dq over dk", dict(dq=_ptr(7)), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", DP_FWD_BAD, ids=[x[0] for x in DP_FWD_BAD])
+def test_fwd_dropout_rejects(fa, name, kw, want):
+    assert _fwd_dp(fa, **kw) == want
+
+
+@pytest.mark.parametrize("name,kw,want", DP_BWD_BAD, ids=[x[0] for x in DP_BWD_BAD])
+def test_bwd_dropout_rejects(fa, name, kw, want):
+    assert _bwd_dp(fa, **kw) == want
+
+
 @pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
 def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd(fa) == fa.FA_ERR_HIP
@@ -251,6 +292,10 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _bwd_kv(fa) == fa.FA_ERR_HIP
     assert _fwd_sp(fa) == fa.FA_ERR_HIP
     assert _bwd_sp(fa) == fa.FA_ERR_HIP
+    assert _fwd_dp(fa) == fa.FA_ERR_HIP
+    assert _fwd_dp(fa, p=0.0) == fa.FA_ERR_HIP
+    assert _fwd_dp(fa, p=float(np.nextafter(np.float32(1), np.float32(0)))) == fa.FA_ERR_HIP
+    assert _bwd_dp(fa) == fa.FA_ERR_HIP
 
 
 def test_python_helpers_refuse_cpu_tensors(fa):
