@@ -114,3 +114,27 @@ def block_mask(B, H, N, keep, seed, block=128):
     g.manual_seed(seed)
     nb = (N + block - 1) // block
     return (torch.rand((B, H, nb, nb), generator=g) < keep).to(torch.uint8)
+
+
+def fp8_inputs(B, H, N, d, seed, q_scale=1.0, v_uniform=False):
+    """OCP E4M3 codes q8, k8, v8 (torch.uint8 [B,H,N,d]) and their dequantisation factors.
+
+    fp32 draws as in make_inputs (N(0,1) times q_scale; V optionally U(-1, 1)),
+    then per tensor: descale = the smallest power of two >= amax / 448, and the
+    code is the E4M3 rounding (to nearest even) of x / descale, so every code is
+    finite and the division is exact.  Returns (q8, k8, v8, (dq, dk, dv)).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = (torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0) if v_uniform else \
+        torch.randn(shape, generator=g, dtype=torch.float32)
+    codes, descales = [], []
+    for x in (q * q_scale, k * q_scale, v * q_scale):
+        amax = float(x.abs().max()) if x.numel() else 0.0
+        ds = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
+        codes.append((x / ds).to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+        descales.append(ds)
+    return codes[0], codes[1], codes[2], tuple(descales)

@@ -399,3 +399,43 @@ def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
             dq[b, h] = scale * (dsz @ k[b, h])
             dk[b, h] = scale * (dsz.T @ q[b, h])
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# 8-bit floating-point inputs.  The pages say FlashAttention 3 adds
+# lower-precision paths where the GPU supports them ("How Flash Attention
+# Works", section "FlashAttention 1 vs 2 vs 3") and fix no format or scaling.
+# The reading taken here:
+#   * q, k and v hold OCP E4M3 codes ("OCP 8-bit Floating Point Specification
+#     (OFP8)", revision 1.0, 2023): one sign bit, four exponent bits with bias
+#     7, three mantissa bits; exponent field 0 encodes the subnormals
+#     m / 8 * 2^-6; the codes with all exponent and mantissa bits set are NaN;
+#     there are no infinities;
+#   * each tensor carries one real dequantisation factor, so the attention
+#     inputs are descale_q * E(q), descale_k * E(k), descale_v * E(v);
+#   * the result is the plain definition on those values: exact attention
+#     and its LSE, computed here in float64.
+# ---------------------------------------------------------------------------
+
+def e4m3_decode(codes):
+    """float64 values of uint8 OCP E4M3 codes (any array shape)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >= 128, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where((c & 127) == 127, np.nan, sign * mag)
+
+
+def attention_forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, scale, causal):
+    """O, LSE of exact attention on dequantised E4M3 inputs ([B, H, N, d] code arrays)."""
+    q = e4m3_decode(_codes(q8)) * float(descale_q)
+    k = e4m3_decode(_codes(k8)) * float(descale_k)
+    v = e4m3_decode(_codes(v8)) * float(descale_v)
+    return attention_forward(q, k, v, scale, causal)
+
+
+def _codes(x):
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.asarray(x, dtype=np.uint8)

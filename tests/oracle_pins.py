@@ -724,6 +724,80 @@ def pin_dropout_finite_differences(orc):
             assert err < 1e-7, f"dropout finite differences grad {which} causal={causal}: {err:.2e}"
 
 
+# ------------------------------------------------------------------ fp8 inputs
+# Reading (the pages name lower-precision paths, no format): q, k, v are OCP
+# E4M3 codes, each tensor with one dequantisation factor; the result is exact
+# attention on the dequantised values.
+def _e4m3_fixture():
+    with open(os.path.join(GOLDEN, "e4m3_values.json")) as f:
+        return {int(c, 16): (math.nan if v is None else v) for c, v in json.load(f)["values"].items()}
+
+
+def pin_e4m3_table(orc):
+    for code, want in _e4m3_fixture().items():
+        got = float(orc.e4m3_decode(np.array([code], dtype=np.uint8))[0])
+        if math.isnan(want):
+            assert math.isnan(got), f"e4m3 code {code:#04x} should be NaN, got {got}"
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), \
+                f"e4m3 code {code:#04x}: {got} != {want}"
+
+
+def pin_e4m3_library(orc):
+    """All 256 codes against torch's float8_e4m3fn (the same OCP format)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "e4m3 NaN codes differ from torch"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "e4m3 values differ from torch"
+
+
+def pin_e4m3_order(orc):
+    pos = orc.e4m3_decode(np.arange(127, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0), "codes 0x00..0x7e must increase strictly"
+    neg = orc.e4m3_decode(np.arange(128, 255, dtype=np.uint8))
+    assert np.array_equal(neg, -pos), "the sign bit must negate"
+
+
+def pin_fp8_bruteforce(orc):
+    """Scalar loops over fixture codes with three different dequantisation factors."""
+    table = {c: v for c, v in _e4m3_fixture().items() if not math.isnan(v) and abs(v) <= 3.0}
+    codes = np.array(sorted(table), dtype=np.uint8)
+    r = _rng(71)
+    for causal, (N, d) in ((False, (5, 3)), (True, (6, 4))):
+        q8, k8, v8 = (codes[r.integers(0, len(codes), (1, 2, N, d))] for _ in range(3))
+        dq, dk, dv, scale = 0.75, 1.25, 0.5, 0.4
+        o, lse = orc.attention_forward_fp8(q8, k8, v8, dq, dk, dv, scale, causal)
+        for h in range(2):
+            q = [[dq * table[int(x)] for x in row] for row in q8[0, h]]
+            k = [[dk * table[int(x)] for x in row] for row in k8[0, h]]
+            v = [[dv * table[int(x)] for x in row] for row in v8[0, h]]
+            bo, bl = _brute_head(q, k, v, scale, causal)
+            _close(o[0, h], bo, 1e-12, f"fp8 brute O causal={causal}")
+            _close(lse[0, h], bl, 1e-12, f"fp8 brute LSE causal={causal}")
+
+
+def pin_fp8_descale_invariances(orc):
+    r = _rng(72)
+    q8, k8, v8 = (r.integers(0, 127, (1, 2, 9, 8)).astype(np.uint8) | (r.integers(0, 2, (1, 2, 9, 8)) * 128).astype(np.uint8)
+                  for _ in range(3))
+    q8[q8 & 127 == 127] = 0x38  # no NaN codes
+    k8[k8 & 127 == 127] = 0x38
+    v8[v8 & 127 == 127] = 0x38
+    base_o, base_l = orc.attention_forward_fp8(q8, k8, v8, 0.01, 0.02, 0.5, 0.3, True)
+    o, l = orc.attention_forward_fp8(q8, k8, v8, 0.01, 0.02, 1.0, 0.3, True)
+    _close(o, 2.0 * base_o, 1e-12, "O is linear in descale_v")
+    _close(l, base_l, 1e-12, "LSE does not see descale_v")
+    o, l = orc.attention_forward_fp8(q8, k8, v8, 0.04, 0.02, 0.5, 0.075, True)
+    _close(o, base_o, 1e-12, "descale_q * 4 with scale / 4")
+    _close(l, base_l, 1e-12, "descale_q * 4 with scale / 4 (LSE)")
+    ones = np.full_like(v8, 0x38)
+    o, _ = orc.attention_forward_fp8(q8, k8, ones, 0.01, 0.02, 0.5, 0.3, False)
+    _close(o, np.full(o.shape, 0.5), 1e-14, "constant V = descale_v * 1")
+
+
 ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pin_constant_v,
             pin_q_zero, pin_causal_row0_and_n1, pin_shift_invariance, pin_permutation,
             pin_online_recurrence, pin_scipy_logsumexp, pin_torch_autograd,
@@ -733,4 +807,5 @@ ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pi
             pin_sparse_all_ones_is_dense, pin_sparse_bruteforce, pin_sparse_block_diagonal,
             pin_sparse_torch_autograd, pin_sparse_finite_differences,
             pin_philox_known_answers, pin_dropout_p0_is_dense, pin_dropout_bruteforce, pin_dropout_keep_rate,
-            pin_dropout_unbiased, pin_dropout_torch_autograd, pin_dropout_finite_differences]
+            pin_dropout_unbiased, pin_dropout_torch_autograd, pin_dropout_finite_differences,
+            pin_e4m3_table, pin_e4m3_library, pin_e4m3_order, pin_fp8_bruteforce, pin_fp8_descale_invariances]

@@ -56,6 +56,12 @@ MUTANTS = {
     "dropout counter transposed": ("words = philox4x32(j >> np.uint64(2), i,", "words = philox4x32(i >> np.uint64(2), j,"),
     "dropout dP without Z": ("dpz = (do[b, h] @ v[b, h].T) * z", "dpz = (do[b, h] @ v[b, h].T)"),
     "dropout dV without Z": ("dv[b, h] = (pr * z).T @ do[b, h]", "dv[b, h] = pr.T @ do[b, h]"),
+    "e4m3 exponent bias 8": ("np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3 subnormals as normals": ("np.where(e == 0, np.ldexp(m / 8.0, -6)", "np.where(e == -1, np.ldexp(m / 8.0, -6)"),
+    "e4m3 subnormal exponent": ("np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
+    "e4m3 NaN code": ("(c & 127) == 127", "(c & 127) == 126"),
+    "fp8 descale_v dropped": ("v = e4m3_decode(_codes(v8)) * float(descale_v)", "v = e4m3_decode(_codes(v8))"),
+    "fp8 k takes descale_q": ("k = e4m3_decode(_codes(k8)) * float(descale_k)", "k = e4m3_decode(_codes(k8)) * float(descale_q)"),
     "kv dropped D term": ("ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))\n            dq[b, h, :a]",
                           "ds = p * dp\n            dq[b, h, :a]"),
 }
