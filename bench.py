@@ -27,9 +27,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention TFLOP/s (fwd, fwd+bwd; causal-adjusted) and % of MI355X bf16 MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}   # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_io_aware_51_amd/csrc/fa_fwd.hip", "exact_io_aware_51_amd/csrc/fa_fwd16.hip",
+                  "exact_io_aware_51_amd/csrc/fa_fwd8.hip",
                   "exact_io_aware_51_amd/csrc/fa_bwd.hip", "exact_io_aware_51_amd/csrc/fa_bwd16.hip",
                   "exact_io_aware_51_amd/csrc/fa_device.h", "exact_io_aware_51_amd/csrc/fa_tile16.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -180,6 +181,42 @@ def time_fwd_only(name, dev, iters=20, warmup=3):
             "shape": f"{w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
+def time_fwd_fp8(name, dev, iters=20, warmup=3):
+    """The forward of workload `name`'s shape on E4M3 inputs (fa_fwd_fp8), against the 8-bit matrix peak."""
+    import math
+
+    import torch
+
+    import exact_io_aware_51_amd as fa
+    from exact_io_aware_51_amd import workloads as W
+    w = W.WORKLOADS[name]
+    q8, k8, v8, ds = W.fp8_inputs(w.B, w.H, w.N, w.d, w.seed, q_scale=w.q_scale, v_uniform=w.v_uniform)
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def run():
+        st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
+                           w.N, w.d, w.scale, int(w.causal), ds[0], ds[1], ds[2], stream)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd_fp8: {fa.fa_status_string(st)}")
+    for _ in range(warmup):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        ev[2 * i].record()
+        run()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)) / iters
+    tf = w.fwd_flops() / (ms * 1e-3) / 1e12
+    assert math.isfinite(float(o.float().abs().max()))
+    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["e4m3"], 4),
+            "shape": f"e4m3 in, bf16 out, B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +337,11 @@ def main():
         fw["c5"] = {"ms": kernels["fwd"]["ms"], "tflops": kernels["fwd"]["tflops"],
                     "frac_of_peak": round(kernels["fwd"]["tflops"] / PEAK_TFLOPS[w.dtype], 4)}
         out["fwd_workloads"] = fw
+        f8 = {}
+        for name in ("c3", "c4"):
+            log(f"bench: forward-only {name} shape on E4M3 inputs")
+            f8[name] = time_fwd_fp8(name, dev)
+        out["fwd_fp8_workloads"] = f8
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

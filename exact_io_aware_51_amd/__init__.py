@@ -2,10 +2,10 @@
 
 The functions named like the C entry points (fa_fwd, fa_bwd, fa_fwd_kv,
 fa_bwd_kv, fa_fwd_sparse, fa_bwd_sparse, fa_fwd_dropout, fa_bwd_dropout,
-fa_bwd_workspace_bytes, ...) take raw device addresses and sizes exactly as
-include/fa.h declares them.  forward(), backward(), forward_kv(),
-backward_kv(), forward_sparse(), backward_sparse(), forward_dropout() and
-backward_dropout() are conveniences for torch tensors:
+fa_fwd_fp8, fa_bwd_workspace_bytes, ...) take raw device addresses and sizes
+exactly as include/fa.h declares them.  forward(), backward(), forward_kv(),
+backward_kv(), forward_sparse(), backward_sparse(), forward_dropout(),
+backward_dropout() and forward_fp8() are conveniences for torch tensors:
 they check shapes, allocate the outputs with torch, pass data_ptr()s and
 torch's current HIP stream, and raise FaError on a non-zero status.  All
 arithmetic happens in the HIP kernels; there is no CPU or PyTorch fallback,
@@ -21,7 +21,8 @@ __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd
            "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
            "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
            "backward_kv", "forward_sparse", "backward_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "forward_dropout", "backward_dropout", "SPARSE_BLOCK", "library_path", "load"]
+           "forward_dropout", "backward_dropout", "fa_fwd_fp8", "forward_fp8", "SPARSE_BLOCK", "library_path",
+           "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 SPARSE_BLOCK = 128  # rows and keys per block of a block-sparse mask (FA_SPARSE_BLOCK)
@@ -32,7 +33,7 @@ _LIB = None
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_status_string", "fa_version")
+           "fa_fwd_fp8", "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -79,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_dropout.restype = i
     lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, f, u64, u32, i, vp]
     lib.fa_bwd_dropout.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, f, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -145,6 +148,10 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes
                    dropout_p, seed, offset, dtype, stream) -> int:
     return load().fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                                  scale, causal, dropout_p, seed, offset, dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, stream) -> int:
+    return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
@@ -372,3 +379,28 @@ def backward_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, scale=Non
     if st != FA_OK:
         raise FaError(st, "fa_bwd_dropout")
     return dq, dk, dv
+
+
+def forward_fp8(q8, k8, v8, descale_q=1.0, descale_k=1.0, descale_v=1.0, scale=None, causal=False, need_lse=True,
+                stream=None):
+    """fa_fwd_fp8 on torch tensors: E4M3 codes (uint8 or float8_e4m3fn) [B, H, N, d] in, bf16 O and fp32 LSE out."""
+    import torch
+    codes = []
+    for t in (q8, k8, v8):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError("tensors must live on a HIP device (no CPU path exists)")
+        if t.dtype == torch.float8_e4m3fn:
+            t = t.view(torch.uint8)
+        if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_contiguous() or t.shape != q8.shape:
+            raise ValueError("q8, k8, v8 must be contiguous [B, H, N, d] E4M3 codes of one shape")
+        codes.append(t)
+    B, H, N, d = q8.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if need_lse else None
+    st = fa_fwd_fp8(codes[0].data_ptr(), codes[1].data_ptr(), codes[2].data_ptr(), o.data_ptr(),
+                    lse.data_ptr() if lse is not None else None, B, H, N, d, scale, int(bool(causal)),
+                    float(descale_q), float(descale_k), float(descale_v), _stream(q8, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return o, lse

@@ -151,6 +151,34 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   return run_fwd(q, k, v, o, lse, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, stream, drop);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, float descale_q, float descale_k, float descale_v, void* stream) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * N >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !std::isfinite(descale_q) || !std::isfinite(descale_k) || !std::isfinite(descale_v))
+    return FA_ERR_INVALID_ARG;
+  const double eff = (double)scale * descale_q * descale_k;  // scale of the raw code products
+  if (!std::isfinite((float)eff) || !std::isfinite((float)eff * 1.4426950408889634f)) return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+  const size_t ti = (size_t)B * H * N * d, to = 2 * ti, lb = (size_t)B * H * N * sizeof(float);
+  const Range ins[3] = {{q, ti}, {k, ti}, {v, ti}};
+  for (const Range& r : ins) {
+    if (overlap({o, to}, r)) return FA_ERR_INVALID_ARG;
+    if (lse && overlap({lse, lb}, r)) return FA_ERR_INVALID_ARG;
+  }
+  if (lse && overlap({o, to}, {lse, lb})) return FA_ERR_INVALID_ARG;
+  fa::FwdProblem p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.B = B; p.H = H; p.Nq = N; p.Nk = N; p.d = d;
+  p.scale = (float)eff; p.causal = causal; p.descale_v = descale_v;
+  (void)hipGetLastError();  // report only this launch's error
+  return hip_status(fa::launch_fwd8(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, fa_dtype dtype) {
   if (check_common(B, H, N, d, 1.0f, 0, (int)dtype) != FA_OK) return 0;
   const size_t need = (size_t)B * H * N * sizeof(float);

@@ -29,7 +29,8 @@ struct FwdProblem {
   float drop_scale;
   float scale;
   int causal;
-  int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16
+  int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16 (launch_fwd8: E4M3 inputs, bf16 o)
+  float descale_v;  // launch_fwd8 only: o = (P v) * descale_v; scale already holds descale_q * descale_k
 };
 
 struct BwdProblem {
@@ -57,6 +58,7 @@ struct BwdProblem {
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s);  // bf16 / fp16 only
+hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s);   // E4M3 q, k, v; bf16 o; Nq = Nk, dense
 // stage: 0 = row sums D, 1 = dK/dV, 2 = dQ
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only

@@ -225,6 +225,33 @@ int fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
                    float dropout_p, unsigned long long seed, unsigned int offset,
                    fa_dtype dtype, void *stream);
 
+/*
+ * Forward pass on 8-bit floating-point inputs.  The pages say FlashAttention 3
+ * adds lower-precision paths where the hardware has them ("How Flash Attention
+ * Works", section "FlashAttention 1 vs 2 vs 3") and fix no format, scaling or
+ * output type; this entry point takes:
+ *   q, k, v : device pointers to uint8 [B,H,N,d] OCP E4M3 codes ("OCP 8-bit
+ *             Floating Point Specification (OFP8)", revision 1.0: sign, 4
+ *             exponent bits with bias 7, 3 mantissa bits, no infinities,
+ *             S.1111.111 = NaN), 16-byte aligned
+ *   descale_q, descale_k, descale_v : one real factor per tensor; the
+ *             attention inputs are descale_x * E4M3(x)
+ *   o       : bf16 [B,H,N,d] output, o = softmax(scale * Q K^T [+ causal]) V
+ *             on the dequantised Q, K, V (rounded to nearest even)
+ *   lse     : fp32 [B,H,N] log-sum-exp of the dequantised scaled scores, or NULL
+ * Q K^T and P V run on the 8-bit matrix cores with fp32 accumulation; the
+ * softmax weights are rounded to E4M3 (round to nearest even, relative error
+ * at most 2^-4 above 2^-6) before they multiply v, which bounds the error of
+ * each output by about 2^-4 * sum_j P_ij |v_jc| beyond the bf16 rounding.
+ * NaN codes propagate.  d in {64, 128}; N >= 1; B*H*N < 2^31; scale and the
+ * factors finite, scale * descale_q * descale_k finite in fp32; causal in
+ * {0, 1}.  Outputs must not overlap inputs.  Errors and stream semantics are
+ * those of fa_fwd.  There is no 8-bit backward pass.
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+               int B, int H, int N, int d, float scale, int causal,
+               float descale_q, float descale_k, float descale_v, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -40,7 +40,8 @@ def _declared():
 def test_header_declares_the_abi():
     assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv",
                                   "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
-                                  "fa_fwd_dropout", "fa_bwd_dropout", "fa_status_string", "fa_version"])
+                                  "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_fp8", "fa_status_string",
+                                  "fa_version"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -281,6 +282,31 @@ def test_bwd_dropout_rejects(fa, name, kw, want):
     assert _bwd_dp(fa, **kw) == want
 
 
+# 8-bit inputs: q, k, v are N*d bytes per head, o twice that (bf16).
+def _fwd8(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, N=256, d=128, scale=0.088,
+             causal=1, dq=0.01, dk=0.02, dv=0.5, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                         a["causal"], a["dq"], a["dk"], a["dv"], a["stream"])
+
+
+FP8_BAD = [
+    ("N=0", dict(N=0), -1), ("d=96", dict(d=96), -2), ("causal=2", dict(causal=2), -1),
+    ("null q", dict(q=None), -1), ("misaligned k", dict(k=_ptr(1, 8)), -1), ("misaligned lse", dict(lse=_ptr(4, 2)), -1),
+    ("inf descale_q", dict(dq=float("inf")), -1), ("nan descale_v", dict(dv=float("nan")), -1),
+    ("scale product overflows", dict(scale=1e30, dq=1e30, dk=1e10), -1),
+    # o is bf16: 2 bytes per element, so it reaches into the next input at twice the input size
+    ("o over v", dict(o=_ptr(2, -2 * 256 * 128)), -1), ("lse over o", dict(lse=_ptr(3, 4)), -1),
+    ("B*H*N too large", dict(B=1 << 16, H=1 << 8, N=1 << 8), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", FP8_BAD, ids=[x[0] for x in FP8_BAD])
+def test_fwd_fp8_rejects(fa, name, kw, want):
+    assert _fwd8(fa, **kw) == want
+
+
 @pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
 def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd(fa) == fa.FA_ERR_HIP
@@ -296,6 +322,8 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd_dp(fa, p=0.0) == fa.FA_ERR_HIP
     assert _fwd_dp(fa, p=float(np.nextafter(np.float32(1), np.float32(0)))) == fa.FA_ERR_HIP
     assert _bwd_dp(fa) == fa.FA_ERR_HIP
+    assert _fwd8(fa) == fa.FA_ERR_HIP
+    assert _fwd8(fa, lse=None, causal=0, d=64, scale=-0.1) == fa.FA_ERR_HIP
 
 
 def test_python_helpers_refuse_cpu_tensors(fa):
