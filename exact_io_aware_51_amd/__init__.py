@@ -2,8 +2,8 @@
 
 The functions named like the C entry points (fa_fwd, fa_bwd, fa_fwd_kv,
 fa_bwd_kv, fa_fwd_sparse, fa_bwd_sparse, fa_fwd_dropout, fa_bwd_dropout,
-fa_fwd_fp8, fa_bwd_workspace_bytes, ...) take raw device addresses and sizes
-exactly as include/fa.h declares them.  forward(), backward(), forward_kv(),
+fa_fwd_fp8, fa_fwd_kv_split, fa_bwd_workspace_bytes, ...) take raw device
+addresses and sizes exactly as include/fa.h declares them.  forward(), backward(), forward_kv(),
 backward_kv(), forward_sparse(), backward_sparse(), forward_dropout(),
 backward_dropout() and forward_fp8() are conveniences for torch tensors:
 they check shapes, allocate the outputs with torch, pass data_ptr()s and
@@ -21,8 +21,8 @@ __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd
            "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
            "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
            "backward_kv", "forward_sparse", "backward_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "forward_dropout", "backward_dropout", "fa_fwd_fp8", "forward_fp8", "SPARSE_BLOCK", "library_path",
-           "load"]
+           "forward_dropout", "backward_dropout", "fa_fwd_fp8", "forward_fp8", "fa_fwd_kv_split",
+           "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "SPARSE_BLOCK", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 SPARSE_BLOCK = 128  # rows and keys per block of a block-sparse mask (FA_SPARSE_BLOCK)
@@ -33,7 +33,8 @@ _LIB = None
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_fwd_fp8", "fa_status_string", "fa_version")
+           "fa_fwd_fp8", "fa_fwd_kv_split", "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint",
+           "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -82,6 +83,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dropout.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, f, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_kv_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i, i, vp, sz, i, vp]
+    lib.fa_fwd_kv_split.restype = i
+    lib.fa_fwd_kv_split_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_kv_split_workspace_bytes.restype = sz
+    lib.fa_fwd_kv_split_hint.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_kv_split_hint.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -152,6 +159,20 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, stream) -> int:
     return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, stream)
+
+
+def fa_fwd_kv_split(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, num_splits, workspace,
+                    workspace_bytes, dtype, stream) -> int:
+    return load().fa_fwd_kv_split(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, num_splits,
+                                  workspace, workspace_bytes, dtype, stream)
+
+
+def fa_fwd_kv_split_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:
+    return load().fa_fwd_kv_split_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+
+
+def fa_fwd_kv_split_hint(B, H, Nq, Nk, d) -> int:
+    return load().fa_fwd_kv_split_hint(B, H, Nq, Nk, d)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
@@ -403,4 +424,27 @@ def forward_fp8(q8, k8, v8, descale_q=1.0, descale_k=1.0, descale_v=1.0, scale=N
                     float(descale_q), float(descale_k), float(descale_v), _stream(q8, stream))
     if st != FA_OK:
         raise FaError(st, "fa_fwd_fp8")
+    return o, lse
+
+
+def forward_kv_split(q, k, v, seqlens_q=None, seqlens_k=None, scale=None, causal=False, num_splits=None,
+                     need_lse=True, stream=None):
+    """fa_fwd_kv_split on torch tensors; num_splits=None takes fa_fwd_kv_split_hint's value."""
+    import torch
+    B, H, Nq, Nk, d = _check_kv(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if num_splits is None:
+        num_splits = fa_fwd_kv_split_hint(B, H, Nq, Nk, d)
+    need = fa_fwd_kv_split_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if need_lse else None
+    sq, sk = _lengths(seqlens_q, B, q.device), _lengths(seqlens_k, B, q.device)
+    st = fa_fwd_kv_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                         lse.data_ptr() if lse is not None else None, B, H, Nq, Nk, d,
+                         sq.data_ptr() if sq is not None else None, sk.data_ptr() if sk is not None else None,
+                         scale, int(bool(causal)), int(num_splits), ws.data_ptr(), ws.numel(), _dtype_code(q),
+                         _stream(q, stream))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_kv_split")
     return o, lse

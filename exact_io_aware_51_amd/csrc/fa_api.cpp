@@ -16,6 +16,8 @@ constexpr int kVersion = 10000;  // 1.0.0
 // Block-sparse kernels keep one mask row or column as bits in LDS: at most
 // 64 x 64 blocks of 128.
 constexpr int kMaxSparseN = 64 * 64 * 128;
+// Key ranges a split-key forward may use.
+constexpr int kMaxSplits = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -77,7 +79,7 @@ int drop_spec(float p, unsigned long long seed, unsigned offset, DropSpec* out) 
 // (batch, head), with optional device arrays of per-sequence lengths.
 int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
             const int* seqlens_q, const int* seqlens_k, const unsigned char* block_mask, float scale, int causal,
-            int dtype, void* stream, const DropSpec& drop = kNoDrop) {
+            int dtype, void* stream, const DropSpec& drop = kNoDrop, int splits = 1, void* part = nullptr) {
   int st = check_shape(B, H, Nq, Nk, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
@@ -96,7 +98,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   }
   if (lse && overlap({o, tq}, {lse, lb})) return FA_ERR_INVALID_ARG;
 
-  fa::FwdProblem p;
+  fa::FwdProblem p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.H = H; p.Nq = Nq; p.Nk = Nk; p.d = d;
   p.seqlens_q = seqlens_q; p.seqlens_k = seqlens_k;
@@ -104,6 +106,7 @@ int run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, in
   p.drop_on = drop.on; p.drop_threshold = drop.threshold; p.drop_seed_lo = drop.seed_lo;
   p.drop_seed_hi = drop.seed_hi; p.drop_offset = drop.offset; p.drop_scale = drop.scale;
   p.scale = scale; p.causal = causal; p.dtype = dtype;
+  p.splits = splits; p.part = static_cast<float*>(part);
   (void)hipGetLastError();  // report only this launch's error
   return hip_status(fa::launch_fwd(p, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -133,6 +136,46 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 int fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk, int d,
               const int* seqlens_q, const int* seqlens_k, float scale, int causal, fa_dtype dtype, void* stream) {
   return run_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype, stream);
+}
+
+size_t fa_fwd_kv_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  if (check_shape(B, H, Nq, Nk, d, 1.0f, 0, FA_BF16) != FA_OK) return 0;
+  if (num_splits < 1 || num_splits > kMaxSplits) return 0;
+  if (num_splits == 1) return 0;
+  const size_t need = (size_t)num_splits * B * H * Nq * (d + 1) * sizeof(float);
+  return (need + 255) & ~(size_t)255;
+}
+
+int fa_fwd_kv_split_hint(int B, int H, int Nq, int Nk, int d) {
+  if (check_shape(B, H, Nq, Nk, d, 1.0f, 0, FA_BF16) != FA_OK) return 1;
+  const long long wgs = (long long)B * H * ((Nq + 127) / 128);
+  const long long tiles = (Nk + 63) / 64;
+  long long s = (2 * 256 + wgs - 1) / wgs;  // about two workgroups per CU
+  const long long by_len = tiles / 16;      // each split at least 16 key tiles (1024 keys)
+  if (s > by_len) s = by_len;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+int fa_fwd_kv_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq, int Nk,
+                    int d, const int* seqlens_q, const int* seqlens_k, float scale, int causal, int num_splits,
+                    void* workspace, size_t workspace_bytes, fa_dtype dtype, void* stream) {
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (num_splits == 1)
+    return run_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype, stream);
+  const int st = check_shape(B, H, Nq, Nk, d, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_fwd_kv_split_workspace_bytes(B, H, Nq, Nk, d, num_splits);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+  const size_t tq = (size_t)B * H * Nq * d * elem_bytes(dtype), tk = (size_t)B * H * Nk * d * elem_bytes(dtype);
+  const size_t sb = (size_t)B * sizeof(int);
+  const Range others[7] = {{q, tq}, {k, tk}, {v, tk}, {o, tq}, {lse, lse ? (size_t)B * H * Nq * sizeof(float) : 0},
+                           {seqlens_q, seqlens_q ? sb : 0}, {seqlens_k, seqlens_k ? sb : 0}};
+  for (const Range& r : others)
+    if (r.p && overlap({workspace, need}, r)) return FA_ERR_WORKSPACE;
+  return run_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype, stream,
+                 kNoDrop, num_splits, workspace);
 }
 
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,

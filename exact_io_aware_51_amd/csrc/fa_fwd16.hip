@@ -51,6 +51,12 @@ struct Fwd16Args {
   int total;
   float c;
   int negate;
+  // SPLIT kernels: key range split s covers tiles [s * split_tiles, (s + 1) * split_tiles)
+  // and writes fp32 partial O [splits][B*H*Nq][D] and LSE [splits][B*H*Nq] instead of o / lse
+  int splits, split_tiles;
+  int rows;  // B * H * Nq
+  float* part_o;
+  float* part_lse;
 };
 
 #ifndef FA16_PRIO
@@ -67,7 +73,7 @@ struct Fwd16Args {
 #define FA_FWD_BN64 64
 #endif
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   constexpr int BN = D == 64 ? FA_FWD_BN64 : 64;  // keys per tile
   constexpr int KB = BN / 32;                      // 32-key blocks per tile
@@ -87,7 +93,12 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(block_id(), a.total);
+  int bid = xcd_remap(block_id(), a.total);
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = __builtin_amdgcn_readfirstlane(bid % a.splits);
+    bid = __builtin_amdgcn_readfirstlane(bid / a.splits);
+  }
   const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
   int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
   if (CAUSAL) qb = a.nqb - 1 - qb;
@@ -109,6 +120,13 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   // key tiles this block visits, and how many leading ones no real row sees masked
   int nt, nt_full;
   query_block_tiles<CAUSAL, BN>(sq, q0, 128, &nt, &nt_full);
+  // split-key kernels visit tiles [tlo, nt) of their own range only
+  int tlo = 0;
+  if constexpr (SPLIT) {
+    tlo = split * a.split_tiles;
+    nt = __builtin_amdgcn_readfirstlane(nt < tlo + a.split_tiles ? nt : tlo + a.split_tiles);
+    nt_full = nt_full < nt ? nt_full : nt;
+  }
   const int lim = key_limit<CAUSAL>(sq, myq);
   const int wlast = qw + 31 + sq.off;  // causal: the last key any row of this wave may see
   // block-sparse: this query block's mask row, packed into bits in LDS; a key
@@ -338,10 +356,11 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   if constexpr (!SPARSE) {
-    if (nt > 0) {  // (nt is block-uniform: every wave takes the same barriers)
-      dma(Kg, 0, KREG);
-      step(0, 1, -1, I0{}, std::false_type{});
-      int j = 1;
+    // tile j sits in stage (j - tlo) & 1; tlo = 0 except in split-key kernels
+    if (nt > tlo) {  // (nt and tlo are block-uniform: every wave takes the same barriers)
+      dma(Kg, BN * tlo, KREG);
+      step(tlo, tlo + 1, -1, I0{}, std::false_type{});
+      int j = tlo + 1;
       for (; j + 1 < nt_full; j += 2) {
         step(j, j + 1, j - 1, I1{}, std::true_type{});
         step(j + 1, j + 2, j, I0{}, std::true_type{});
@@ -351,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
         ++j;
       }
       for (; j < nt; ++j) {
-        if (j & 1)
+        if ((j - tlo) & 1)
           step(j, j + 1, j - 1, I1{}, std::false_type{});
         else
           step(j, j + 1, j - 1, I0{}, std::false_type{});
@@ -360,7 +379,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
       wait_vmem();
       __builtin_amdgcn_s_barrier();
       if (!CAUSAL || BN * (nt - 1) <= wlast) {
-        if ((nt - 1) & 1)
+        if ((nt - 1 - tlo) & 1)
           pv(1);
         else
           pv(0);
@@ -412,6 +431,27 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 
   // padding rows and rows that see no key store O = 0, LSE = -inf
   l = halves_sum(l);
+  if constexpr (SPLIT) {
+    // this key range's normalised partial output and its LSE, both fp32
+    if (myq < Nq) {
+      const bool real = myq < sq.lq && l > 0.0f;
+      const float inv = real ? 1.0f / l : 0.0f;
+      const size_t row = (size_t)split * a.rows + (size_t)bh * Nq + myq;
+      float* prow = a.part_o + row * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * mb + 8 * g + 4 * h;
+          f32x4 o4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o4[u] = real ? oacc[mb][4 * g + u] * inv : 0.0f;
+          *reinterpret_cast<f32x4*>(prow + d0) = o4;
+        }
+      if (h == 0) a.part_lse[row] = real ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+    }
+    return;
+  }
   if (myq < Nq) {
     const bool real = myq < sq.lq && l > 0.0f;
     const float inv = real ? (DROP ? a.drop.scale : 1.0f) / l : 0.0f;
@@ -431,7 +471,37 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   }
 }
 
-template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
+// Merge of split-key partials: one wave per row.  With M = max_s LSE_s and
+// w_s = exp(LSE_s - M): LSE = M + ln sum_s w_s and O = sum_s w_s O_s / sum_s w_s,
+// the same rescale the online softmax applies tile by tile.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* part_o, const float* part_lse, int splits,
+                                                          int rows, T* o, float* lse) {
+  constexpr int PER = D / 64;  // channels per lane
+  const int lane = thread_id() & 63;
+  const int row = __builtin_amdgcn_readfirstlane(block_id() * 4 + (thread_id() >> 6));
+  if (row >= rows) return;
+  float mx = -__builtin_inff();
+  for (int sp = 0; sp < splits; ++sp) mx = __builtin_fmaxf(mx, part_lse[(size_t)sp * rows + row]);
+  float acc[PER] = {}, wsum = 0.0f;
+  if (mx > -__builtin_inff()) {
+    for (int sp = 0; sp < splits; ++sp) {
+      const float ls = part_lse[(size_t)sp * rows + row];
+      const float w = ls > -__builtin_inff() ? fast_exp2((ls - mx) * kLog2e) : 0.0f;
+      wsum += w;
+      const float* po = part_o + ((size_t)sp * rows + row) * D + lane * PER;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += w * po[u];
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  T* orow = o + (size_t)row * D + lane * PER;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) orow[u] = (T)(acc[u] * inv);
+  if (lse != nullptr && lane == 0) lse[row] = wsum > 0.0f ? mx + __builtin_log2f(wsum) * kLn2 : -__builtin_inff();
+}
+
+template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
 static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   Fwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
@@ -446,6 +516,21 @@ static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   const float sc = p.scale;
   a.negate = sc < 0.0f;
   a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
+  a.splits = 1; a.split_tiles = 0; a.rows = p.B * p.H * p.Nq; a.part_o = nullptr; a.part_lse = nullptr;
+  if constexpr (SPLIT) {
+    a.splits = p.splits;
+    const int tiles = (p.Nk + 63) / 64;
+    a.split_tiles = (tiles + p.splits - 1) / p.splits;
+    a.part_o = p.part;
+    a.part_lse = p.part + (size_t)p.splits * a.rows * D;
+    a.total *= p.splits;
+    hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, false, false, true>), dim3(a.total), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((split_merge_kernel<T, D>), dim3((a.rows + 3) / 4), dim3(256), 0, stream, a.part_o,
+                       a.part_lse, a.splits, a.rows, reinterpret_cast<T*>(p.o), p.lse);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -457,9 +542,16 @@ static hipError_t launch_fwd16_s(const FwdProblem& p, hipStream_t s) {
   return p.causal ? launch_fwd16_t<T, 128, true, SPARSE, DROP>(p, s) : launch_fwd16_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
-// (block sparsity and dropout are not combined: the API rejects that)
+// (block sparsity, dropout and key splitting are not combined: the API rejects that)
 template <typename T>
 static hipError_t launch_fwd16_d(const FwdProblem& p, hipStream_t s) {
+  if (p.splits > 1) {
+    if (p.d == 64)
+      return p.causal ? launch_fwd16_t<T, 64, true, false, false, true>(p, s)
+                      : launch_fwd16_t<T, 64, false, false, false, true>(p, s);
+    return p.causal ? launch_fwd16_t<T, 128, true, false, false, true>(p, s)
+                    : launch_fwd16_t<T, 128, false, false, false, true>(p, s);
+  }
   if (p.drop_on) return launch_fwd16_s<T, false, true>(p, s);
   return p.block_mask != nullptr ? launch_fwd16_s<T, true, false>(p, s) : launch_fwd16_s<T, false, false>(p, s);
 }

@@ -31,6 +31,11 @@ struct FwdProblem {
   int causal;
   int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16 (launch_fwd8: E4M3 inputs, bf16 o)
   float descale_v;  // launch_fwd8 only: o = (P v) * descale_v; scale already holds descale_q * descale_k
+  // key splitting (16-bit only; splits <= 1: none): split s handles key tiles
+  // [s * ceil(tiles / splits), ...) and writes fp32 partials into `part`
+  // ([splits][B*H*Nq][d] outputs, then [splits][B*H*Nq] LSEs); a merge pass writes o / lse
+  int splits;
+  float* part;
 };
 
 struct BwdProblem {

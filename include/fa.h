@@ -160,6 +160,34 @@ int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o,
               float scale, int causal, fa_dtype dtype, void *stream);
 
 /*
+ * Split-key forward, for few query rows against many keys (decoding against a
+ * key cache): with B * H * ceil(Nq / 128) workgroups only, most compute units
+ * would idle.  The key range is cut into num_splits pieces of whole 64-key
+ * tiles; each (batch, head, 128-query block, piece) runs the fa_fwd_kv
+ * algorithm on its keys and writes an fp32 partial output and log-sum-exp into
+ * `workspace`, and a merge pass combines them with the same rescale the online
+ * softmax applies tile by tile ("How Flash Attention Works", section "Online
+ * Softmax Without the Full Score Matrix"):
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * Arguments, layout, lengths and causal alignment are those of fa_fwd_kv; the
+ * result equals fa_fwd_kv's up to rounding order, and fa_bwd_kv accepts it.
+ *   num_splits : 1 .. 256; 1 is fa_fwd_kv itself (workspace unused, may be
+ *                NULL).  fa_fwd_kv_split_hint suggests a value.
+ *   workspace  : device buffer of at least fa_fwd_kv_split_workspace_bytes()
+ *                bytes, 16-byte aligned, not overlapping any other argument;
+ *                contents on entry ignored, clobbered on exit.
+ * 16-bit dtypes only: FA_F32 with num_splits > 1 returns FA_ERR_UNSUPPORTED.
+ */
+size_t fa_fwd_kv_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+int fa_fwd_kv_split_hint(int B, int H, int Nq, int Nk, int d);
+int fa_fwd_kv_split(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Nq, int Nk, int d,
+                    const int *seqlens_q, const int *seqlens_k,
+                    float scale, int causal, int num_splits,
+                    void *workspace, size_t workspace_bytes,
+                    fa_dtype dtype, void *stream);
+
+/*
  * Block-sparse attention.  The pages name a block-sparse extension studied
  * beside the dense algorithm as a separate configuration ("FlashAttention"
  * glossary entry, its definition) and fix no mask format; this one is:

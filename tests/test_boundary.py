@@ -40,7 +40,8 @@ def _declared():
 def test_header_declares_the_abi():
     assert _declared() == sorted(["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv",
                                   "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
-                                  "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_fp8", "fa_status_string",
+                                  "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_fp8", "fa_fwd_kv_split",
+                                  "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "fa_status_string",
                                   "fa_version"])
 
 
@@ -282,6 +283,43 @@ def test_bwd_dropout_rejects(fa, name, kw, want):
     assert _bwd_dp(fa, **kw) == want
 
 
+# Split-key forward: B=1, H=2, Nq=4, Nk=4096, d=128, 8 splits -> 8 * 8 * 129 * 4 bytes of workspace.
+def _fwd_split(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, Nq=4, Nk=4096, d=128,
+             sq=None, sk=_ptr(11), scale=0.088, causal=1, ns=8, ws=_ptr(9), wsb=1 << 20, dtype=fa.FA_BF16,
+             stream=None)
+    a.update(kw)
+    return fa.fa_fwd_kv_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                              a["sq"], a["sk"], a["scale"], a["causal"], a["ns"], a["ws"], a["wsb"], a["dtype"],
+                              a["stream"])
+
+
+def test_split_workspace_and_hint(fa):
+    assert fa.fa_fwd_kv_split_workspace_bytes(1, 2, 4, 4096, 128, 8) == 8 * 8 * 129 * 4
+    assert fa.fa_fwd_kv_split_workspace_bytes(1, 2, 4, 4096, 128, 1) == 0
+    assert fa.fa_fwd_kv_split_workspace_bytes(1, 2, 4, 4096, 128, 0) == 0
+    assert fa.fa_fwd_kv_split_workspace_bytes(1, 2, 4, 4096, 96, 8) == 0
+    assert fa.fa_fwd_kv_split_hint(1, 8, 1, 32768, 128) == 32      # at least 1024 keys per split
+    assert fa.fa_fwd_kv_split_hint(4, 32, 1, 8192, 128) == 4       # about 512 workgroups
+    assert fa.fa_fwd_kv_split_hint(1, 8, 1, 1024, 128) == 1
+    assert fa.fa_fwd_kv_split_hint(4, 32, 8192, 8192, 64) == 1     # already thousands of workgroups
+    assert fa.fa_fwd_kv_split_hint(1, 1, 1, 64, 64) == 1
+
+
+SPLIT_BAD = [
+    ("0 splits", dict(ns=0), -1), ("257 splits", dict(ns=257), -1), ("fp32 split", dict(dtype=0), -2),
+    ("null workspace", dict(ws=None), -3), ("small workspace", dict(wsb=4096), -3),
+    ("misaligned workspace", dict(ws=_ptr(9, 8)), -3), ("workspace over k", dict(ws=_ptr(1, 64)), -3),
+    ("workspace over lengths", dict(ws=_ptr(11, -64)), -3), ("d=80", dict(d=80), -2), ("Nk=0", dict(Nk=0), -1),
+    ("o over q", dict(o=_ptr(0, 32)), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", SPLIT_BAD, ids=[x[0] for x in SPLIT_BAD])
+def test_fwd_kv_split_rejects(fa, name, kw, want):
+    assert _fwd_split(fa, **kw) == want
+
+
 # 8-bit inputs: q, k, v are N*d bytes per head, o twice that (bf16).
 def _fwd8(fa, **kw):
     a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, N=256, d=128, scale=0.088,
@@ -323,6 +361,8 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd_dp(fa, p=float(np.nextafter(np.float32(1), np.float32(0)))) == fa.FA_ERR_HIP
     assert _bwd_dp(fa) == fa.FA_ERR_HIP
     assert _fwd8(fa) == fa.FA_ERR_HIP
+    assert _fwd_split(fa) == fa.FA_ERR_HIP
+    assert _fwd_split(fa, ns=1, ws=None) == fa.FA_ERR_HIP
     assert _fwd8(fa, lse=None, causal=0, d=64, scale=-0.1) == fa.FA_ERR_HIP
 
 
