@@ -71,13 +71,29 @@ __device__ inline void reads_ahead() {
 // dP^T_j = V_j dO^T, then forms dS^T_j while the matrix cores accumulate
 // dQ^T += K_{j-1}^T dS^T_{j-1}.  LDS: K in three stages (K_{j-1}, K_j and the
 // one being loaded), V in two.
-#ifndef FA_DQ_OCC128
-#define FA_DQ_OCC128 1
+// dQ kernel, dense d = 128 (no dropout, no block mask): two waves per SIMD
+// (256 VGPRs each) with each tile's dQ products issued in its own step and no
+// extra read-ahead schedule.  Carrying dS into the next step (the schedule of
+// d = 64 and of the dropout / block-sparse kernels) needs ~300 VGPRs and so
+// one wave per SIMD, which measured 9% slower on the c5 backward.
+#ifndef FA_DQ_TWO_WAVES
+#define FA_DQ_TWO_WAVES 1
 #endif
+#ifndef FA_DQ_READAHEAD
+#define FA_DQ_READAHEAD 0
+#endif
+template <int D, bool SPARSE, bool DROP>
+struct DqShape {
+  static constexpr bool TWO = FA_DQ_TWO_WAVES && D == 128 && !SPARSE && !DROP;
+  static constexpr int OCC = D == 64 || TWO ? 2 : 1;
+  static constexpr int AHEAD = TWO ? FA_DQ_READAHEAD : FA_BWD_READAHEAD;
+};
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(Bwd16Args a) {
+__global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_kernel(Bwd16Args a) {
   using M = Mma<T>;
+  constexpr bool NOPIPE = DqShape<D, SPARSE, DROP>::TWO;
+  constexpr int AHEAD = DqShape<D, SPARSE, DROP>::AHEAD;
   using TL = Tile16<D>;
   using Frag = typename M::Frag;
   constexpr int KSTEPS = D / 16;
@@ -203,13 +219,11 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
           s = M::mma(tile16_row_frag<T>(smem, krow[ks] + ko), qf[ks], s);
           p = M::mma(tile16_row_frag<T>(smem, vrow[ks] + vo), dof[ks], p);
         }
-#if FA_BWD_READAHEAD
-        reads_ahead<2 * KSTEPS, 1, FA_BWD_READAHEAD>();
-#endif
+        if constexpr (AHEAD > 0) reads_ahead<2 * KSTEPS, 1, (AHEAD > 0 ? AHEAD : 1)>();
 #if FA_DQ_PRIO
         __builtin_amdgcn_s_setprio(0);
 #endif
-        if (kb == 0 && prev) dq_prev(kps);
+        if (!NOPIPE && kb == 0 && prev) dq_prev(kps);
         const int tk = t0 - 32 * kb;
         // dropout: dP of a dropped weight is 0, of a kept one dP / (1 - p)
         u32x4v w[4];
@@ -232,7 +246,8 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
 #pragma unroll
         for (int t = 0; t < 2; ++t) dsf[kb][t] = acc_frag<T>(p, t);
       }
-    } else if (prev) {
+      if (NOPIPE) dq_prev(ks3);
+    } else if (!NOPIPE && prev) {
       dq_prev(kps);
     }
   };
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
       }
       wait_vmem();
       __builtin_amdgcn_s_barrier();
-      if (!CAUSAL || 64 * (nt - 1) <= wlast) dq_prev((nt - 1) % 3);
+      if (!NOPIPE && (!CAUSAL || 64 * (nt - 1) <= wlast)) dq_prev((nt - 1) % 3);
     }
   } else {
     // Only live tiles are visited, in increasing order; step t uses K stage
@@ -290,7 +305,7 @@ __global__ __launch_bounds__(256, D == 128 ? FA_DQ_OCC128 : 2) void dq16_kernel(
       }
       wait_vmem();
       __builtin_amdgcn_s_barrier();
-      if (!CAUSAL || 64 * jp <= wlast) dq_prev((t - 1) % 3);
+      if (!NOPIPE && (!CAUSAL || 64 * jp <= wlast)) dq_prev((t - 1) % 3);
     }
   }
 
