@@ -181,6 +181,66 @@ def time_fwd_only(name, dev, iters=20, warmup=3):
             "shape": f"{w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
+def _gfx_clocks_mhz():
+    """Current GFX clock of every XCD from amd-smi (MHz), or [] if it cannot be read."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=15)
+        data = json.loads(r.stdout)
+    except Exception:  # noqa: BLE001 - best effort: a missing tool only drops the field
+        return []
+    out = []
+
+    def walk(x):
+        if isinstance(x, dict):
+            for key, val in x.items():
+                if key.startswith("gfx_") and isinstance(val, dict) and isinstance(val.get("clk"), dict):
+                    v = val["clk"].get("value")
+                    if isinstance(v, (int, float)):
+                        out.append(float(v))
+                else:
+                    walk(val)
+        elif isinstance(x, list):
+            for val in x:
+                walk(val)
+    walk(data)
+    return out
+
+
+def clock_under_load(name, dev, seconds=3.0):
+    """Mean GFX clock (MHz) sampled with amd-smi while workload `name`'s forward runs back to back."""
+    import threading
+
+    import torch
+
+    from exact_io_aware_51_amd import workloads as W
+    w = W.WORKLOADS[name]
+    r = Runner(w, dev)
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            c = _gfx_clocks_mhz()
+            if not c:
+                return
+            samples.append(sum(c) / len(c))
+    r.fwd()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        r.fwd()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=20)
+    if len(samples) < 2:
+        return None
+    busy = samples[1:]  # the first sample may predate the load
+    return {"workload": f"{name} forward", "gfx_mhz_mean": round(sum(busy) / len(busy), 1), "samples": len(busy),
+            "source": "amd-smi metric --clock (mean over XCDs)"}
+
+
 def time_fwd_fp8(name, dev, iters=20, warmup=3):
     """The forward of workload `name`'s shape on E4M3 inputs (fa_fwd_fp8), against the 8-bit matrix peak."""
     import math
@@ -342,6 +402,12 @@ def main():
             log(f"bench: forward-only {name} shape on E4M3 inputs")
             f8[name] = time_fwd_fp8(name, dev)
         out["fwd_fp8_workloads"] = f8
+        log("bench: shader clock under the c4 forward")
+        clk = clock_under_load("c4", dev)
+        if clk is not None:
+            clk["c4_frac_of_peak_at_this_clock"] = round(
+                fw["c4"]["tflops"] / (PEAK_TFLOPS["bf16"] * clk["gfx_mhz_mean"] / 2400.0), 4)
+        out["clock"] = clk
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
