@@ -290,6 +290,32 @@ def attention_forward_sparse(q, k, v, scale, causal, block_mask, block=128):
     return o, lse
 
 
+def attention_forward_sparse_rows(q, k, v, scale, causal, block_mask, b, h, rows, block=128):
+    """O and LSE for selected query rows of one (b, h) slice under a block mask (spot checks at any size).
+
+    Row i sees key j iff its mask block (i // block, j // block) is kept and,
+    causal, j <= i; the row is the softmax over those keys alone.
+    """
+    qh, kh, vh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h])
+    n = kh.shape[0]
+    bm = np.asarray(block_mask)[b, h].astype(bool)
+    keys = np.arange(n)
+    o = np.zeros((len(rows), vh.shape[1]))
+    lse = np.full(len(rows), -np.inf)
+    for t, i in enumerate(int(r) for r in rows):
+        seen = bm[i // block, keys // block]
+        if causal:
+            seen &= keys <= i
+        if not seen.any():
+            continue
+        s = scale * (kh[seen] @ qh[i])
+        m = np.max(s)
+        e = np.exp(s - m)
+        lse[t] = m + np.log(np.sum(e))
+        o[t] = (e / np.sum(e)) @ vh[seen]
+    return o, lse
+
+
 def attention_backward_sparse(q, k, v, do, scale, causal, block_mask, block=128):
     """dQ, dK, dV of L = sum(dO * O) for the block-sparse forward above."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)

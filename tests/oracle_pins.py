@@ -724,6 +724,23 @@ def pin_dropout_finite_differences(orc):
             assert err < 1e-7, f"dropout finite differences grad {which} causal={causal}: {err:.2e}"
 
 
+def pin_sparse_rows_match_full(orc):
+    """The per-row sparse sampler equals rows of the full sparse oracle (random masks, an empty block row)."""
+    r = _rng(61)
+    q, k, v = _qkv(61, 1, 2, 23, 3)
+    for causal in (False, True):
+        m = (r.random((1, 2, 6, 6)) < 0.5).astype(np.uint8)
+        m[0, 1, 2, :] = 0
+        o, lse = orc.attention_forward_sparse(q, k, v, 0.7, causal, m, block=4)
+        for h in range(2):
+            rows = [0, 5, 8, 9, 17, 22]
+            so, sl = orc.attention_forward_sparse_rows(q, k, v, 0.7, causal, m, 0, h, rows, block=4)
+            _close(so, o[0, h, rows], 1e-13, f"sparse rows O causal={causal}")
+            assert np.array_equal(np.isinf(sl), np.isinf(lse[0, h, rows])), "sparse rows: empty rows differ"
+            fin = ~np.isinf(sl)
+            _close(sl[fin], lse[0, h, rows][fin], 1e-13, f"sparse rows LSE causal={causal}")
+
+
 # ------------------------------------------------------------------ fp8 inputs
 # Reading (the pages name lower-precision paths, no format): q, k, v are OCP
 # E4M3 codes, each tensor with one dequantisation factor; the result is exact
@@ -805,7 +822,7 @@ ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pi
             pin_kv_reduces_to_square, pin_kv_worked_example, pin_kv_bruteforce, pin_kv_decode_and_empty,
             pin_kv_padding_invariance, pin_kv_torch_autograd, pin_kv_finite_differences,
             pin_sparse_all_ones_is_dense, pin_sparse_bruteforce, pin_sparse_block_diagonal,
-            pin_sparse_torch_autograd, pin_sparse_finite_differences,
+            pin_sparse_torch_autograd, pin_sparse_finite_differences, pin_sparse_rows_match_full,
             pin_philox_known_answers, pin_dropout_p0_is_dense, pin_dropout_bruteforce, pin_dropout_keep_rate,
             pin_dropout_unbiased, pin_dropout_torch_autograd, pin_dropout_finite_differences,
             pin_e4m3_table, pin_e4m3_library, pin_e4m3_order, pin_fp8_bruteforce, pin_fp8_descale_invariances]

@@ -56,6 +56,7 @@ MUTANTS = {
     "dropout counter transposed": ("words = philox4x32(j >> np.uint64(2), i,", "words = philox4x32(i >> np.uint64(2), j,"),
     "dropout dP without Z": ("dpz = (do[b, h] @ v[b, h].T) * z", "dpz = (do[b, h] @ v[b, h].T)"),
     "dropout dV without Z": ("dv[b, h] = (pr * z).T @ do[b, h]", "dv[b, h] = pr.T @ do[b, h]"),
+    "sparse rows mask transposed": ("seen = bm[i // block, keys // block]", "seen = bm[keys // block, i // block]"),
     "e4m3 exponent bias 8": ("np.ldexp(1.0 + m / 8.0, e - 7)", "np.ldexp(1.0 + m / 8.0, e - 8)"),
     "e4m3 subnormals as normals": ("np.where(e == 0, np.ldexp(m / 8.0, -6)", "np.where(e == -1, np.ldexp(m / 8.0, -6)"),
     "e4m3 subnormal exponent": ("np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
