@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0: dropout, 8-bit forward, split-key forward
 // Block-sparse kernels keep one mask row or column as bits in LDS: at most
 // 64 x 64 blocks of 128.
 constexpr int kMaxSparseN = 64 * 64 * 128;

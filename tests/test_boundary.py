@@ -56,7 +56,7 @@ def test_status_strings(fa):
         s = fa.fa_status_string(st)
         assert s and s != "unknown status"
     assert fa.fa_status_string(12345) == "unknown status"
-    assert fa.fa_version() == 10000
+    assert fa.fa_version() == 10100
 
 
 def test_workspace_bytes(fa):
