@@ -166,6 +166,7 @@ int fa_fwd_kv_split(const void* q, const void* k, const void* v, void* o, float*
   const int st = check_shape(B, H, Nq, Nk, d, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * ((Nq + 127) / 128) * num_splits >= (1LL << 31)) return FA_ERR_INVALID_ARG;  // grid size
   const size_t need = fa_fwd_kv_split_workspace_bytes(B, H, Nq, Nk, d, num_splits);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
   const size_t tq = (size_t)B * H * Nq * d * elem_bytes(dtype), tk = (size_t)B * H * Nk * d * elem_bytes(dtype);

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D>(goff, wave, lane);
   auto dma = [&](const char* g, int row0, int region) __attribute__((always_inline)) {
-    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, tile_bytes(sq.lk - row0, 64, TL::ROWB));
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i) lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
   };
@@ -405,8 +405,8 @@ __global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
   float lse_next = 0.0f, d_next = 0.0f;  // wave 0 stages the next tile's per-row values
   auto fetch = [&](int i, int stage) __attribute__((always_inline)) {
     const int row0 = 64 * i;
-    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lq - row0) * TL::ROWB);
-    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lq - row0) * TL::ROWB);
+    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, tile_bytes(sq.lq - row0, 64, TL::ROWB));
+    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, tile_bytes(sq.lq - row0, 64, TL::ROWB));
 #pragma unroll
     for (int r = 0; r < TL::ROUNDS; ++r) {
       lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * 4 + wave) * 1024, goff[r]);

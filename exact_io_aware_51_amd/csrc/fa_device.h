@@ -190,6 +190,14 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Byte count for the descriptor of one tile of `tile_rows` rows when
+// `rows_left` rows remain before the end of the sequence: loads past it return
+// zeros.  Clamped to the tile, so the 32-bit count cannot wrap however long
+// the sequence is (the tile's base address is formed in 64 bits by the caller).
+__device__ inline uint32_t tile_bytes(int rows_left, int tile_rows, int row_bytes) {
+  return (uint32_t)(rows_left < tile_rows ? rows_left : tile_rows) * (uint32_t)row_bytes;
+}
+
 __device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }

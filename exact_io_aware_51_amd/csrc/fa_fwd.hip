@@ -157,8 +157,8 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
   }
   u32x4 kreg[L::PER_THREAD], vreg[L::PER_THREAD];
   auto load_tile = [&](int j) {
-    const uint32_t base = (uint32_t)(j * kFwdBN) * L::ROWB;
-    const uint32_t left = (uint32_t)(sq.lk - j * kFwdBN) * L::ROWB;
+    const size_t base = (size_t)j * kFwdBN * L::ROWB;
+    const uint32_t left = tile_bytes(sq.lk - j * kFwdBN, kFwdBN, L::ROWB);
     const auto rk = buffer_rsrc(Kb + base, left);
     const auto rv = buffer_rsrc(Vb + base, left);
 #pragma unroll

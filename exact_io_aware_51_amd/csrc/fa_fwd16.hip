@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   uint32_t goff[TL::ROUNDS];
   tile16_load_offsets<D, BN>(goff, wave, lane);
   auto dma = [&](const char* g, int row0, int region) __attribute__((always_inline)) {
-    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, tile_bytes(sq.lk - row0, BN, TL::ROWB));
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i)
       lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
     goff[i] = r * TL::ROWB + ((pc ^ TL::sw(r)) << 4);
   }
   auto dma = [&](const char* g, int row0, int region) __attribute__((always_inline)) {
-    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, (uint32_t)(sq.lk - row0) * TL::ROWB);
+    const auto rs = buffer_rsrc(g + (size_t)row0 * TL::ROWB, tile_bytes(sq.lk - row0, BN, TL::ROWB));
 #pragma unroll
     for (int i = 0; i < TL::ROUNDS; ++i) lds_load16(rs, smem + region + (i * 4 + wave) * 1024, goff[i]);
   };

@@ -177,6 +177,7 @@ int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o,
  *                bytes, 16-byte aligned, not overlapping any other argument;
  *                contents on entry ignored, clobbered on exit.
  * 16-bit dtypes only: FA_F32 with num_splits > 1 returns FA_ERR_UNSUPPORTED.
+ * B * H * ceil(Nq / 128) * num_splits must stay below 2^31 (the launch grid).
  */
 size_t fa_fwd_kv_split_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 int fa_fwd_kv_split_hint(int B, int H, int Nq, int Nk, int d);

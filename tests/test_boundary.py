@@ -312,6 +312,7 @@ SPLIT_BAD = [
     ("misaligned workspace", dict(ws=_ptr(9, 8)), -3), ("workspace over k", dict(ws=_ptr(1, 64)), -3),
     ("workspace over lengths", dict(ws=_ptr(11, -64)), -3), ("d=80", dict(d=80), -2), ("Nk=0", dict(Nk=0), -1),
     ("o over q", dict(o=_ptr(0, 32)), -1),
+    ("grid past 2^31", dict(B=1 << 13, H=1 << 10, Nq=1, Nk=64, ns=256, wsb=1 << 62), -1),  # 2^23 heads x 256 splits
 ]
 
 

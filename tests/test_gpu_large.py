@@ -85,3 +85,66 @@ def test_backward_n65536():
     assert np.all(dk_sum <= 1e-3 * dk_abs + 1e-3), f"sum_j dK_j not 0: worst {np.max(dk_sum / (dk_abs + 1e-30)):.2e}"
     dv_err = np.abs(dv64.sum(axis=0) - do64.sum(axis=0))
     assert np.all(dv_err <= 1e-3 * np.abs(dv64).sum(axis=0) + 1e-2), f"sum_j dV_j != sum_i dO_i: {dv_err.max():.3e}"
+
+
+# ------------------------------------------------------------------ addressing past 2^32 bytes per head
+# With Q = K = 0 every score is 0, so each row's softmax is uniform: O = (sum of the V
+# rows) / Nk and LSE = ln Nk exactly, whatever the length.  V (or dO) is zero except
+# "probe" rows set to 1, placed around the row counts where a 32-bit byte count or
+# offset per head would wrap (2^24 rows of 256 bytes, 2^23 rows of 512 bytes); a
+# tile that is read short, or from the wrong place, changes the result.
+
+def _probe_rows(n, wrap):
+    rows = {0, 1, n - 1, wrap - 1, wrap, wrap + 1}
+    rows |= set(range(n - wrap - 64, n - wrap + 64))  # the tile whose remaining byte count wraps to a few KiB
+    return sorted(r for r in rows if 0 <= r < n)
+
+
+@pytest.mark.parametrize("path", ["kv", "split", "fp32"])
+def test_key_addressing_beyond_4gib_per_head(path):
+    dev = device()
+    dtype = torch.float32 if path == "fp32" else torch.bfloat16
+    d = 128
+    wrap = (1 << 32) // (d * (4 if path == "fp32" else 2))  # rows per 4 GiB
+    nk = wrap + 1000
+    announce("long keys", path, nk)
+    q = torch.zeros((1, 1, 1, d), dtype=dtype, device=dev)
+    k = torch.zeros((1, 1, nk, d), dtype=dtype, device=dev)
+    v = torch.zeros((1, 1, nk, d), dtype=dtype, device=dev)
+    probes = _probe_rows(nk, wrap)
+    v[0, 0, probes] = 1.0
+    if path == "split":
+        o, lse = fa.forward_kv_split(q, k, v, num_splits=64)
+    else:
+        o, lse = fa.forward_kv(q, k, v)
+    torch.cuda.synchronize()
+    want = len(probes) / nk
+    got = o.double().cpu().numpy()
+    assert np.allclose(got, want, rtol=1e-2, atol=0), f"{path}: O {got.min():.6e}..{got.max():.6e}, want {want:.6e}"
+    assert abs(float(lse) - np.log(nk)) <= 1e-4, f"{path}: LSE {float(lse)} vs {np.log(nk)}"
+    del k, v
+
+
+def test_query_addressing_beyond_4gib_per_head():
+    """The backward streams Q and dO tiles past 2^24 rows of 256 bytes: dV_j = (sum_i dO_i) / Nk exactly."""
+    dev = device()
+    d, nk = 128, 64
+    wrap = (1 << 32) // (d * 2)
+    nq = wrap + 1000
+    announce("long queries", nq)
+    q = torch.zeros((1, 1, nq, d), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((1, 1, nk, d), dtype=torch.bfloat16, device=dev)
+    v = torch.randn((1, 1, nk, d), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(dev)
+    do = torch.zeros_like(q)
+    probes = _probe_rows(nq, wrap)
+    do[0, 0, probes] = 1.0
+    o, lse = fa.forward_kv(q, k, v)
+    dq, dk, dv = fa.backward_kv(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    want = len(probes) / nk
+    got = dv.double().cpu().numpy()
+    assert np.allclose(got, want, rtol=1e-2, atol=0), f"dV {got.min():.6e}..{got.max():.6e}, want {want:.6e}"
+    assert float(dq.abs().max()) == 0.0 and float(dk.abs().max()) == 0.0
+    o_want = v.double().mean(dim=2, keepdim=True).cpu().numpy()
+    o_rows = o[0, 0, probes].double().cpu().numpy()
+    assert np.allclose(o_rows, o_want[0, 0], rtol=1e-2, atol=1e-3), "O of probe rows is not mean(V)"
