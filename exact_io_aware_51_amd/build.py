@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd16.hip", "fa_fwd8.hip", "fa_bwd.hip", "fa_bwd16.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd16.hip", "fa_fwd8.hip", "fa_decode.hip", "fa_bwd.hip", "fa_bwd16.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are switched off for all device code.

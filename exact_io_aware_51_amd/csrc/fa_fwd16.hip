@@ -527,9 +527,7 @@ static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, false, false, true>), dim3(a.total), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((split_merge_kernel<T, D>), dim3((a.rows + 3) / 4), dim3(256), 0, stream, a.part_o,
-                       a.part_lse, a.splits, a.rows, reinterpret_cast<T*>(p.o), p.lse);
-    return hipGetLastError();
+    return launch_split_merge(p, stream);
   }
   hipLaunchKernelGGL((fwd16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -542,9 +540,25 @@ static hipError_t launch_fwd16_s(const FwdProblem& p, hipStream_t s) {
   return p.causal ? launch_fwd16_t<T, 128, true, SPARSE, DROP>(p, s) : launch_fwd16_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
+template <typename T, int D>
+static hipError_t launch_split_merge_t(const FwdProblem& p, hipStream_t s) {
+  const int rows = p.B * p.H * p.Nq;
+  const float* po = p.part;
+  const float* pl = p.part + (size_t)p.splits * rows * D;
+  hipLaunchKernelGGL((split_merge_kernel<T, D>), dim3((rows + 3) / 4), dim3(256), 0, s, po, pl, p.splits, rows,
+                     reinterpret_cast<T*>(p.o), p.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const FwdProblem& p, hipStream_t s) {
+  if (p.dtype == 1) return p.d == 64 ? launch_split_merge_t<_Float16, 64>(p, s) : launch_split_merge_t<_Float16, 128>(p, s);
+  return p.d == 64 ? launch_split_merge_t<__bf16, 64>(p, s) : launch_split_merge_t<__bf16, 128>(p, s);
+}
+
 // (block sparsity, dropout and key splitting are not combined: the API rejects that)
 template <typename T>
 static hipError_t launch_fwd16_d(const FwdProblem& p, hipStream_t s) {
+  if (p.splits > 1 && p.Nq == 1) return launch_decode(p, s);  // one query row per head
   if (p.splits > 1) {
     if (p.d == 64)
       return p.causal ? launch_fwd16_t<T, 64, true, false, false, true>(p, s)

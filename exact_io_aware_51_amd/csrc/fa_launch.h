@@ -64,6 +64,9 @@ struct BwdProblem {
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s);  // bf16 / fp16 only
 hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s);   // E4M3 q, k, v; bf16 o; Nq = Nk, dense
+// split keys (p.splits > 1, 16-bit): partials into p.part, then the merge into o / lse
+hipError_t launch_decode(const FwdProblem& p, hipStream_t s);       // Nq == 1
+hipError_t launch_split_merge(const FwdProblem& p, hipStream_t s);
 // stage: 0 = row sums D, 1 = dK/dV, 2 = dQ
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only

@@ -169,6 +169,9 @@ int fa_bwd_kv(const void *q, const void *k, const void *v, const void *o,
  * softmax applies tile by tile ("How Flash Attention Works", section "Online
  * Softmax Without the Full Score Matrix"):
  *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * With Nq = 1 (one query row per head, plain decoding) the pieces run a
+ * streaming kernel instead of the tiled one: no LDS staging, every wave reads
+ * whole consecutive key rows straight into registers.
  * Arguments, layout, lengths and causal alignment are those of fa_fwd_kv; the
  * result equals fa_fwd_kv's up to rounding order, and fa_bwd_kv accepts it.
  *   num_splits : 1 .. 256; 1 is fa_fwd_kv itself (workspace unused, may be
