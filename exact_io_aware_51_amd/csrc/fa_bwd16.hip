@@ -335,8 +335,15 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
 // The four accumulators (dK^T, dV^T) and the stationary fragments need about
 // 280 VGPRs, so one wave per SIMD runs this kernel; the element-wise work of
 // one half overlaps the matrix ops of the other inside the wave.
+// d = 64 (no dropout): the kernel fits 256 VGPRs without spills, so two waves
+// share each SIMD; measured 1.5x faster than one.  d = 128 needs ~450 and the
+// dropout instantiations spill at 256: one wave.
+#ifndef FA_DKDV_OCC64
+#define FA_DKDV_OCC64 2
+#endif
+
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, 1) void dkdv16_kernel(Bwd16Args a) {
+__global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void dkdv16_kernel(Bwd16Args a) {
   using M = Mma<T>;
   using TL = Tile16<D>;
   using Frag = typename M::Frag;
