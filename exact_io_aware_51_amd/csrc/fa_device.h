@@ -167,6 +167,11 @@ __device__ inline float halves_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of registers o .. o + 7 of an accumulator, pairwise (dependency depth 3).
+__device__ inline float sum8(const f32x16& x, int o) {
+  return ((x[o] + x[o + 1]) + (x[o + 2] + x[o + 3])) + ((x[o + 4] + x[o + 5]) + (x[o + 6] + x[o + 7]));
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (blockIdx % 8 = XCD).
 // Renumber them so that consecutive logical indices share an XCD (and so its
 // L2): XCD x receives logical blocks [x*q + min(x, r), ...) in order.

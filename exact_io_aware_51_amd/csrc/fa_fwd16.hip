@@ -257,10 +257,9 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
           for (int t = 0; t < 2; ++t) {
             f32x16 p8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, negm));
-              rs += p8[8 * t + e];
-            }
+            for (int e = 0; e < 8; ++e) p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, negm));
+            const float s8 = sum8(p8, 8 * t);  // pairwise: dependency depth 3, not a chain of 8
+            rs = (kb == 0 && t == 0) ? s8 : rs + s8;
             drop_mask(p8, kb, t, k0);
             pf[kb][t] = acc_frag<T>(p8, t);
           }
@@ -331,8 +330,9 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
             p = ro <= t0 - 32 * kb ? p : 0.0f;
           }
           sc[kb][r] = p;
-          rs += p;
         }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) rs += sum8(sc[kb], 0) + sum8(sc[kb], 8);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll

@@ -36,6 +36,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
+// Transposing 8-bit LDS read.  Like lds_tr16 (fa_tile16.h), the pointer is
+// restrict-qualified so the read is not ordered behind the direct loads in
+// flight into other LDS stages; each step waits for those loads explicitly
+// before any wave reads the stage they fill.
+__device__ __attribute__((always_inline)) inline i32x2 lds_tr8(const char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+}
+
 struct Fwd8Args {
   const void* q;
   const void* k;
@@ -170,8 +178,7 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
     i32x2 r[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      r[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2*)(smem + vaddr[mb] + stage * TL::BYTES + 16 * t * TL::ROWB));
+      r[t] = lds_tr8(smem + vaddr[mb] + stage * TL::BYTES + 16 * t * TL::ROWB);
     return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
   };
 
@@ -229,10 +236,9 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
           for (int t = 0; t < 2; ++t) {
             f32x16 p8;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, negm));
-              rs += p8[8 * t + e];
-            }
+            for (int e = 0; e < 8; ++e) p8[8 * t + e] = fast_exp2(__builtin_fmaf(sc[kb][8 * t + e], c, negm));
+            const float s8 = sum8(p8, 8 * t);
+            rs = (kb == 0 && t == 0) ? s8 : rs + s8;
             pack_half(p8, kb, t);
           }
         if (any_lane(rs > 256.0f)) {
@@ -289,8 +295,9 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
           const int ro = 8 * (r >> 2) + (r & 3);
           const float p = fast_exp2(__builtin_fmaf(sc[kb][r], c, negm));
           sc[kb][r] = ro <= t0 - 32 * kb ? p : 0.0f;
-          rs += sc[kb][r];
         }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) rs += sum8(sc[kb], 0) + sum8(sc[kb], 8);
       if (need) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;

@@ -67,11 +67,22 @@ __device__ inline typename Mma<T>::Frag tile16_row_frag(const char* smem, uint32
   return __builtin_bit_cast(typename Mma<T>::Frag, *reinterpret_cast<const u32x4*>(smem + addr));
 }
 
+// Transposing 16-bit LDS read.  The compiler cannot tell an LDS read from the
+// direct (buffer -> LDS) loads still in flight into other stages, and without
+// alias information it waits for all of them (vmcnt(0)) before the read, which
+// stalls each pipeline step on the loads it has just issued for the next tile.
+// The restrict-qualified pointer gives the read that information.  Every kernel
+// waits for its direct loads explicitly (vmcnt(0), then a barrier, since other
+// waves read what each wave loads) before reading the stage they filled.
+__device__ __attribute__((always_inline)) inline i16x4 lds_tr16(const char* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
 template <typename T, int D>
 __device__ inline typename Mma<T>::Frag tile16_tr_frag(const char* smem, uint32_t a0, uint32_t a1, int off) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + a0 + off));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + a1 + off));
+  const i16x4 lo = lds_tr16(smem + a0 + off);
+  const i16x4 hi = lds_tr16(smem + a1 + off);
   const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(typename Mma<T>::Frag, both);
 }
