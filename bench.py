@@ -83,6 +83,69 @@ def traffic_for(kernel):
     return entry.get("hbm_bytes_per_launch")
 
 
+STEP_KERNELS = {"fwd16_kernel": "fwd", "bwd_pre_kernel": "bwd_rowsum", "dkdv16_kernel": "bwd_dkdv",
+                "dq16_kernel": "bwd_dq"}
+
+
+def _counter_per_dispatch(run_dir, counter):
+    """{kernel name: mean per-dispatch value of `counter`} from a rocprofv3 --pmc CSV run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    per = {}  # (kernel, dispatch) -> summed value
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (kname, _), v in per.items():
+        out.setdefault(kname, []).append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def write_traffic(prof_dir, w):
+    """Build profiles/traffic.json from four rocprofv3 --pmc runs under prof_dir:
+    pmc_traffic_FETCH_SIZE, pmc_traffic_WRITE_SIZE (the step, bench.py --no-fwd-workloads) and
+    pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE (bench.py --copy-calibration 1024)."""
+    copy_bytes = 1024 << 20
+    cf = _counter_per_dispatch(os.path.join(prof_dir, "pmc_copy_FETCH_SIZE"), "FETCH_SIZE")
+    cw = _counter_per_dispatch(os.path.join(prof_dir, "pmc_copy_WRITE_SIZE"), "WRITE_SIZE")
+    copy_name = next(k for k in cf if "copyBuffer" in k)
+    fetch_factor = copy_bytes / (cf[copy_name] * 1024.0)
+    write_factor = copy_bytes / (cw[copy_name] * 1024.0)
+    sf = _counter_per_dispatch(os.path.join(prof_dir, "pmc_traffic_FETCH_SIZE"), "FETCH_SIZE")
+    sw = _counter_per_dispatch(os.path.join(prof_dir, "pmc_traffic_WRITE_SIZE"), "WRITE_SIZE")
+    models = kernel_models(w)
+    kernels = {}
+    for kname, fkib in sf.items():
+        stage = next((v for k, v in STEP_KERNELS.items() if k in kname), None)
+        if stage is None:
+            continue
+        wkib = sw.get(kname, 0.0)
+        kernels[stage] = {"kernel_symbol": kname, "fetch_kib_per_dispatch": round(fkib, 1),
+                          "write_kib_per_dispatch": round(wkib, 1),
+                          "hbm_bytes_per_launch": int(round(fkib * 1024 * fetch_factor + wkib * 1024 * write_factor)),
+                          "algorithmic_bytes_per_launch": models[stage]["bytes"]}
+    t = {"source_digest": source_digest(),
+         "workload": f"{w.name}: {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}",
+         "calibration": {"copy_kernel": copy_name, "copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
+                         "copy_fetch_kib": round(cf[copy_name], 1), "copy_write_kib": round(cw[copy_name], 1),
+                         "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
+         "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    for stage, e in kernels.items():
+        log(f"{stage}: fetch {e['fetch_kib_per_dispatch']} KiB, write {e['write_kib_per_dispatch']} KiB, "
+            f"HBM {e['hbm_bytes_per_launch'] / 1e6:.1f} MB vs algorithmic {e['algorithmic_bytes_per_launch'] / 1e6:.1f} MB")
+    log(f"wrote {TRAFFIC_FILE} (factors {fetch_factor:.4f} / {write_factor:.4f})")
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle on whole heads of the same workload until `seconds` have passed."""
     import numpy as np
@@ -290,7 +353,13 @@ def main():
                     help="diagnostic: time only the forward kernel of this workload (c1..c5), one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="diagnostic: run a plain device copy of MIB MiB five times (counter calibration)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="write profiles/traffic.json from the rocprofv3 --pmc runs under DIR (no GPU needed)")
     args = ap.parse_args()
+    if args.traffic_from:
+        from exact_io_aware_51_amd import workloads as W
+        write_traffic(args.traffic_from, W.WORKLOADS[args.workload])
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

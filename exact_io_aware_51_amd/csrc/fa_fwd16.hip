@@ -66,7 +66,7 @@ struct Fwd16Args {
 #define FA16_SPEC 1
 #endif
 #ifndef FA16_SCHED
-#define FA16_SCHED 8
+#define FA16_SCHED 4
 #endif
 
 #ifndef FA_FWD_BN64
