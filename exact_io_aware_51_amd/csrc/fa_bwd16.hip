@@ -528,31 +528,15 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
   if constexpr (!SPARSE) {
     if (first < nt) {
       fetch(first, 0);
+      // The LDS stage alternates with the tile; it is a runtime value here.
+      // With compile-time stages (two steps per iteration) the compiler kept
+      // the dK/dV accumulators in two alternating register sets and, short of
+      // registers, issued every LDS read just before its product; one step
+      // per iteration keeps one assignment and lets the reads run ahead.
       int i = first;
-      for (; i < nt && i < full0; ++i) {
-        if ((i - first) & 1)
-          step(i, i + 1, I1{}, std::false_type{});
-        else
-          step(i, i + 1, I0{}, std::false_type{});
-      }
-      // mask-free tiles, two at a time (constant LDS offsets)
-      for (; i + 1 < full1; i += 2) {
-        if ((i - first) & 1) {
-          step(i, i + 1, I1{}, std::true_type{});
-          step(i + 1, i + 2, I0{}, std::true_type{});
-        } else {
-          step(i, i + 1, I0{}, std::true_type{});
-          step(i + 1, i + 2, I1{}, std::true_type{});
-        }
-      }
-      for (; i < nt; ++i) {
-        const bool full = i < full1;
-        if ((i - first) & 1) {
-          if (full) step(i, i + 1, I1{}, std::true_type{}); else step(i, i + 1, I1{}, std::false_type{});
-        } else {
-          if (full) step(i, i + 1, I0{}, std::true_type{}); else step(i, i + 1, I0{}, std::false_type{});
-        }
-      }
+      for (; i < nt && i < full0; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
+      for (; i < full1; ++i) step(i, i + 1, (i - first) & 1, std::true_type{});
+      for (; i < nt; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
     }
   } else {
     // Only live query tiles are visited, in increasing order, alternating
