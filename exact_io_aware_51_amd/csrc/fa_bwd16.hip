@@ -262,8 +262,13 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
       // tile 0 owes no dQ product yet: generic step
       step(0, 1, -1, 0, 0, std::false_type{});
       int j = 1;
-      // mask-free steps, six at a time so that every LDS offset is a constant
-      for (; j + 5 < nt_full; j += 6) {
+      // mask-free steps, six at a time so that every LDS offset is a constant.
+      // Only where two waves share a SIMD (256 VGPRs): with the offsets as
+      // runtime values those kernels spill.  One-wave kernels (d = 128 with
+      // dropout) take the runtime-stage loop below, which keeps one register
+      // assignment for the accumulators and lets the LDS reads run ahead.
+      constexpr bool UNROLL6 = DqShape<D, SPARSE, DROP>::OCC == 2;
+      for (; UNROLL6 && j + 5 < nt_full; j += 6) {
         step(j, j + 1, j - 1, I1{}, I1{}, std::true_type{});
         step(j + 1, j + 2, j, I2{}, I0{}, std::true_type{});
         step(j + 2, j + 3, j + 1, I0{}, I1{}, std::true_type{});
