@@ -109,9 +109,8 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(block_id(), a.total);
-  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
-  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
+  int bh, qb;
+  block_order(block_id(), a.total, a.nblk, CAUSAL, &bh, &qb);
   if (CAUSAL) qb = a.nblk - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;
@@ -367,9 +366,8 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  const int bid = xcd_remap(block_id(), a.total);
-  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nblk);
-  const int kblk = __builtin_amdgcn_readfirstlane(bid - bh * a.nblk);
+  int bh, kblk;  // under the causal mask key block 0 is seen by the most query tiles
+  block_order(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
   const int kb0 = kblk * 128;
   const int kw = kb0 + 32 * wave;
   const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);

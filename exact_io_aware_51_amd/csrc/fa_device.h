@@ -189,6 +189,30 @@ __device__ inline int xcd_remap(int bid, int total) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// Head and rank of a workgroup in a grid of nblk blocks per head over
+// total / nblk heads.  Rank 0 is the block with the most tiles under the
+// causal mask; a kernel maps it to its own block index.
+//  * equal-cost blocks (no causal mask): xcd_remap order, so each XCD's L2
+//    serves few heads;
+//  * causal: ranks in order across all heads (rank = bid / heads, head =
+//    bid % heads), longest first everywhere.  Renumbering by head instead left
+//    each XCD with several heads in a row, each longest-first only within
+//    itself, so short blocks took slots early and the longest ran last
+//    (c5-shape forward: makespan 102 tile-times vs 70 in a list-scheduling
+//    model of one XCD).  With dispatch round-robin over the XCDs (bid % 8),
+//    a head count that is a multiple of 8 still keeps each head on one XCD.
+__device__ inline void block_order(int bid, int total, int nblk, bool by_rank, int* bh, int* rank) {
+  if (by_rank) {
+    const int heads = total / nblk;
+    *rank = __builtin_amdgcn_readfirstlane(bid / heads);
+    *bh = __builtin_amdgcn_readfirstlane(bid - *rank * heads);
+  } else {
+    const int b = xcd_remap(bid, total);
+    *bh = __builtin_amdgcn_readfirstlane(b / nblk);
+    *rank = __builtin_amdgcn_readfirstlane(b - *bh * nblk);
+  }
+}
+
 // Buffer resource over `bytes` bytes starting at `base`: raw buffer loads at
 // offsets at or beyond `bytes` return zeros, which pads ragged tiles for free.
 __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {

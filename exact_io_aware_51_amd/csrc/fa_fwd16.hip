@@ -93,14 +93,16 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   const int h = lane >> 5, col = lane & 31;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  int bid = xcd_remap(block_id(), a.total);
-  int split = 0;
+  int split = 0, bh, qb;
   if constexpr (SPLIT) {
+    int bid = xcd_remap(block_id(), a.total);
     split = __builtin_amdgcn_readfirstlane(bid % a.splits);
     bid = __builtin_amdgcn_readfirstlane(bid / a.splits);
+    bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
+    qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
+  } else {
+    block_order(block_id(), a.total, a.nqb, CAUSAL, &bh, &qb);
   }
-  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
-  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;

@@ -105,9 +105,8 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
   const int h = lane >> 5, col = lane & 31;
   const int N = a.N;
 
-  const int bid = xcd_remap(block_id(), a.total);
-  const int bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
-  int qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
+  int bh, qb;
+  block_order(block_id(), a.total, a.nqb, CAUSAL, &bh, &qb);
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;
