@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
   const int Nq = a.Nq, Nk = a.Nk;
 
   int bh, qb;
-  block_order(block_id(), a.total, a.nblk, CAUSAL, &bh, &qb);
+  block_order<32 * DqShape<D, SPARSE, DROP>::OCC>(block_id(), a.total, a.nblk, CAUSAL, &bh, &qb);
   if (CAUSAL) qb = a.nblk - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
   const int Nq = a.Nq, Nk = a.Nk;
 
   int bh, kblk;  // under the causal mask key block 0 is seen by the most query tiles
-  block_order(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
+  block_order<((D == 64 && !DROP) ? 32 * FA_DKDV_OCC64 : 32)>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
   const int kb0 = kblk * 128;
   const int kw = kb0 + 32 * wave;
   const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     bh = __builtin_amdgcn_readfirstlane(bid / a.nqb);
     qb = __builtin_amdgcn_readfirstlane(bid - bh * a.nqb);
   } else {
-    block_order(block_id(), a.total, a.nqb, CAUSAL, &bh, &qb);
+    block_order<(D == 64 ? 96 : 64)>(block_id(), a.total, a.nqb, CAUSAL, &bh, &qb);  // 3 (d = 64) or 2 workgroups per CU
   }
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int q0 = qb * 128;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
   const int N = a.N;
 
   int bh, qb;
-  block_order(block_id(), a.total, a.nqb, CAUSAL, &bh, &qb);
+  block_order<64>(block_id(), a.total, a.nqb, CAUSAL, &bh, &qb);
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int q0 = qb * 128;
   const int qw = q0 + wave * 32;
