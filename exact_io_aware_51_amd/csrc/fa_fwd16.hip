@@ -211,14 +211,18 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
   // sits in K stage KST, V_jp in V stage KST ^ 1.
   auto step = [&](int j, int jn, int jp, auto kst_tag, auto full_tag) __attribute__((always_inline)) {
     constexpr int KST = decltype(kst_tag)::value;
-    constexpr bool FULL = decltype(full_tag)::value;  // unmasked, and tile jp was done
+    // mode 1: unmasked, and tile jp was done (speculative exponentials);
+    // mode 2: unmasked first tile (maximum first, nothing owed); mode 0: masked
+    constexpr int MODE = decltype(full_tag)::value;
+    constexpr bool FULL = MODE == 1;
+    constexpr bool NOMASK = MODE != 0;
     wait_vmem();
     __builtin_amdgcn_s_barrier();
     if (jn < nt) dma(Kg, BN * jn, KREG + (KST ^ 1) * TL::BYTES);
     dma(Vg, BN * j, VREG + KST * TL::BYTES);
 
     const int k0 = BN * j;
-    const bool act = FULL || !CAUSAL || k0 <= wlast;
+    const bool act = NOMASK || !CAUSAL || k0 <= wlast;
     const bool prev = FULL || (jp >= 0 && (!CAUSAL || BN * jp <= wlast));
     if (act) {
 #if FA16_PRIO
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
         for (int r = 0; r < 16; ++r) {
           const int ro = 8 * (r >> 2) + (r & 3);
           float x = sc[kb][r];
-          if constexpr (!FULL) x = ro <= t0 - 32 * kb ? x : -__builtin_inff();
+          if constexpr (!NOMASK) x = ro <= t0 - 32 * kb ? x : -__builtin_inff();
           xs[16 * kb + r] = x;
         }
       // 3-input max tree over the lane's scores
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
       mx = __builtin_fmaxf(mx, xs[KB * 16 - 1]);
       mx = halves_max(mx);
       float mt = mx * c;
-      if constexpr (!FULL) mt = mx > -__builtin_inff() ? mt : -__builtin_inff();
+      if constexpr (!NOMASK) mt = mx > -__builtin_inff() ? mt : -__builtin_inff();
       const bool need = any_lane(mt > m + 8.0f);
       const float mnew = need ? __builtin_fmaxf(m, mt) : m;
       const float alpha = fast_exp2(m - mnew);
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(__builtin_fmaf(sc[kb][r], c, negm));
-          if constexpr (!FULL) {
+          if constexpr (!NOMASK) {
             const int ro = 8 * (r >> 2) + (r & 3);
             p = ro <= t0 - 32 * kb ? p : 0.0f;
           }
@@ -357,25 +361,29 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   if constexpr (!SPARSE) {
     // tile j sits in stage (j - tlo) & 1; tlo = 0 except in split-key kernels
     if (nt > tlo) {  // (nt and tlo are block-uniform: every wave takes the same barriers)
       dma(Kg, BN * tlo, KREG);
-      step(tlo, tlo + 1, -1, I0{}, std::false_type{});
+      if (tlo < nt_full)
+        step(tlo, tlo + 1, -1, I0{}, I2{});
+      else
+        step(tlo, tlo + 1, -1, I0{}, I0{});
       int j = tlo + 1;
       for (; j + 1 < nt_full; j += 2) {
-        step(j, j + 1, j - 1, I1{}, std::true_type{});
-        step(j + 1, j + 2, j, I0{}, std::true_type{});
+        step(j, j + 1, j - 1, I1{}, I1{});
+        step(j + 1, j + 2, j, I0{}, I1{});
       }
       if (j < nt_full) {
-        step(j, j + 1, j - 1, I1{}, std::true_type{});
+        step(j, j + 1, j - 1, I1{}, I1{});
         ++j;
       }
       for (; j < nt; ++j) {
         if ((j - tlo) & 1)
-          step(j, j + 1, j - 1, I1{}, std::false_type{});
+          step(j, j + 1, j - 1, I1{}, I0{});
         else
-          step(j, j + 1, j - 1, I0{}, std::false_type{});
+          step(j, j + 1, j - 1, I0{}, I0{});
       }
       // the last tile's P still owes its V product
       wait_vmem();
@@ -396,27 +404,30 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     if (j < nt) {
       dma(Kg, BN * j, KREG);
       int jp = -1, jn = next(j);
-      step(j, jn, jp, I0{}, std::false_type{});
+      if (j < nt_full)
+        step(j, jn, jp, I0{}, I2{});
+      else
+        step(j, jn, jp, I0{}, I0{});
       jp = j; j = jn;
       int par = 1;  // stage parity of the next step
       while (j < nt_full) {
         jn = next(j);
-        step(j, jn, jp, I1{}, std::true_type{});
+        step(j, jn, jp, I1{}, I1{});
         jp = j; j = jn;
         if (j >= nt_full) {
           par = 0;
           break;
         }
         jn = next(j);
-        step(j, jn, jp, I0{}, std::true_type{});
+        step(j, jn, jp, I0{}, I1{});
         jp = j; j = jn;
       }
       for (; j < nt; par ^= 1) {
         jn = next(j);
         if (par)
-          step(j, jn, jp, I1{}, std::false_type{});
+          step(j, jn, jp, I1{}, I0{});
         else
-          step(j, jn, jp, I0{}, std::false_type{});
+          step(j, jn, jp, I0{}, I0{});
         jp = j; j = jn;
       }
       // the last visited tile's P still owes its V product (stage par ^ 1)
