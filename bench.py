@@ -32,6 +32,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_io_aware_51_amd/csrc/fa_fwd.hip", "exact_io_aware_51_amd/csrc/fa_fwd16.hip",
                   "exact_io_aware_51_amd/csrc/fa_fwd8.hip", "exact_io_aware_51_amd/csrc/fa_decode.hip",
                   "exact_io_aware_51_amd/csrc/fa_bwd.hip", "exact_io_aware_51_amd/csrc/fa_bwd16.hip",
+                  "exact_io_aware_51_amd/csrc/fa_bwd16_drop.hip", "exact_io_aware_51_amd/build.py",
                   "exact_io_aware_51_amd/csrc/fa_device.h", "exact_io_aware_51_amd/csrc/fa_tile16.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

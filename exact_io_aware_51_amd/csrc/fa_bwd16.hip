@@ -625,16 +625,22 @@ static hipError_t launch_dkdv16_s(const BwdProblem& p, hipStream_t s) {
                   : launch_dkdv16_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
+#ifndef FA_BWD16_DROPOUT_UNIT
 // (block sparsity and dropout are not combined: the API rejects that)
 template <typename T>
 static hipError_t launch_dkdv16_d(const BwdProblem& p, hipStream_t s) {
-  if (p.drop_on) return launch_dkdv16_s<T, false, true>(p, s);
+  if (p.drop_on) return launch_dkdv16_drop(p, s);
   return p.block_mask ? launch_dkdv16_s<T, true, false>(p, s) : launch_dkdv16_s<T, false, false>(p, s);
 }
 
 hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s) {
   return p.dtype == 1 ? launch_dkdv16_d<_Float16>(p, s) : launch_dkdv16_d<__bf16>(p, s);
 }
+#else
+hipError_t launch_dkdv16_drop(const BwdProblem& p, hipStream_t s) {
+  return p.dtype == 1 ? launch_dkdv16_s<_Float16, false, true>(p, s) : launch_dkdv16_s<__bf16, false, true>(p, s);
+}
+#endif
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dq16_t(const BwdProblem& p, hipStream_t stream) {
@@ -650,14 +656,20 @@ static hipError_t launch_dq16_s(const BwdProblem& p, hipStream_t s) {
   return p.causal ? launch_dq16_t<T, 128, true, SPARSE, DROP>(p, s) : launch_dq16_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
+#ifndef FA_BWD16_DROPOUT_UNIT
 template <typename T>
 static hipError_t launch_dq16_d(const BwdProblem& p, hipStream_t s) {
-  if (p.drop_on) return launch_dq16_s<T, false, true>(p, s);
+  if (p.drop_on) return launch_dq16_drop(p, s);
   return p.block_mask ? launch_dq16_s<T, true, false>(p, s) : launch_dq16_s<T, false, false>(p, s);
 }
 
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s) {
   return p.dtype == 1 ? launch_dq16_d<_Float16>(p, s) : launch_dq16_d<__bf16>(p, s);
 }
+#else
+hipError_t launch_dq16_drop(const BwdProblem& p, hipStream_t s) {
+  return p.dtype == 1 ? launch_dq16_s<_Float16, false, true>(p, s) : launch_dq16_s<__bf16, false, true>(p, s);
+}
+#endif
 
 }  // namespace fa

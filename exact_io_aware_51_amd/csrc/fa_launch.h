@@ -71,5 +71,8 @@ hipError_t launch_split_merge(const FwdProblem& p, hipStream_t s);
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only
 hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s);  // bf16 / fp16 only
+// the dropout instantiations (fa_bwd16_drop.hip, a separate compilation unit)
+hipError_t launch_dq16_drop(const BwdProblem& p, hipStream_t s);
+hipError_t launch_dkdv16_drop(const BwdProblem& p, hipStream_t s);
 
 }  // namespace fa
