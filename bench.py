@@ -30,6 +30,7 @@ METRIC = "attention TFLOP/s (fwd, fwd+bwd; causal-adjusted) and % of MI355X bf16
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3, "e4m3": 5000.0}   # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_io_aware_51_amd/csrc/fa_fwd.hip", "exact_io_aware_51_amd/csrc/fa_fwd16.hip",
+                  "exact_io_aware_51_amd/csrc/fa_fwd16_d128.hip",
                   "exact_io_aware_51_amd/csrc/fa_fwd8.hip", "exact_io_aware_51_amd/csrc/fa_decode.hip",
                   "exact_io_aware_51_amd/csrc/fa_bwd.hip", "exact_io_aware_51_amd/csrc/fa_bwd16.hip",
                   "exact_io_aware_51_amd/csrc/fa_bwd16_drop.hip", "exact_io_aware_51_amd/build.py",

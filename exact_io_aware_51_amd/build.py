@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd16.hip", "fa_fwd8.hip", "fa_decode.hip", "fa_bwd.hip", "fa_bwd16.hip",
-           "fa_bwd16_drop.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd16.hip", "fa_fwd16_d128.hip", "fa_fwd8.hip", "fa_decode.hip",
+           "fa_bwd.hip", "fa_bwd16.hip", "fa_bwd16_drop.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -28,12 +28,14 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 DEVICE_FLAGS += ["-fno-honor-nans", "-mno-amdgpu-ieee"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
-# Per-source flags.  The backward kernels are scheduled with LLVM's max-ILP
-# strategy: measured on MI355X, dQ +2.9% and dK/dV +0.9-2.4% on the c5
-# backward, d = 64 dK/dV +2.8%.  Their dropout instantiations (17% slower under
-# it) are a unit of their own, fa_bwd16_drop.hip, and keep the default, as
-# does the forward, under which the d = 64 forward is 4% faster.
-SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source flags.  The backward kernels and the d = 128 forward are
+# scheduled with LLVM's max-ILP strategy: measured on MI355X, dQ +2.5% and
+# dK/dV +2.5% on the c5 backward, d = 64 dK/dV +2.4%, the c5 forward +3.9%.
+# The dropout backward (17% slower under it) and the d = 64 forward (4%
+# slower) keep the default: fa_bwd16_drop.hip and fa_fwd16_d128.hip compile
+# those parts of fa_bwd16.hip / fa_fwd16.hip as units of their own.
+SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:

@@ -546,13 +546,20 @@ static hipError_t launch_fwd16_t(const FwdProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename T, bool SPARSE, bool DROP>
-static hipError_t launch_fwd16_s(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64)
-    return p.causal ? launch_fwd16_t<T, 64, true, SPARSE, DROP>(p, s) : launch_fwd16_t<T, 64, false, SPARSE, DROP>(p, s);
-  return p.causal ? launch_fwd16_t<T, 128, true, SPARSE, DROP>(p, s) : launch_fwd16_t<T, 128, false, SPARSE, DROP>(p, s);
+// Every 16-bit forward variant for one head size D.  (Block sparsity,
+// dropout and key splitting are not combined: the API rejects that.)
+template <typename T, int D>
+static hipError_t launch_fwd16_dd(const FwdProblem& p, hipStream_t s) {
+  const bool c = p.causal;
+  if (p.splits > 1)
+    return c ? launch_fwd16_t<T, D, true, false, false, true>(p, s) : launch_fwd16_t<T, D, false, false, false, true>(p, s);
+  if (p.drop_on) return c ? launch_fwd16_t<T, D, true, false, true>(p, s) : launch_fwd16_t<T, D, false, false, true>(p, s);
+  if (p.block_mask != nullptr)
+    return c ? launch_fwd16_t<T, D, true, true, false>(p, s) : launch_fwd16_t<T, D, false, true, false>(p, s);
+  return c ? launch_fwd16_t<T, D, true, false, false>(p, s) : launch_fwd16_t<T, D, false, false, false>(p, s);
 }
 
+#ifndef FA_FWD16_D128_UNIT
 template <typename T, int D>
 static hipError_t launch_split_merge_t(const FwdProblem& p, hipStream_t s) {
   const int rows = p.B * p.H * p.Nq;
@@ -568,23 +575,17 @@ hipError_t launch_split_merge(const FwdProblem& p, hipStream_t s) {
   return p.d == 64 ? launch_split_merge_t<__bf16, 64>(p, s) : launch_split_merge_t<__bf16, 128>(p, s);
 }
 
-// (block sparsity, dropout and key splitting are not combined: the API rejects that)
-template <typename T>
-static hipError_t launch_fwd16_d(const FwdProblem& p, hipStream_t s) {
-  if (p.splits > 1 && p.Nq == 1) return launch_decode(p, s);  // one query row per head
-  if (p.splits > 1) {
-    if (p.d == 64)
-      return p.causal ? launch_fwd16_t<T, 64, true, false, false, true>(p, s)
-                      : launch_fwd16_t<T, 64, false, false, false, true>(p, s);
-    return p.causal ? launch_fwd16_t<T, 128, true, false, false, true>(p, s)
-                    : launch_fwd16_t<T, 128, false, false, false, true>(p, s);
-  }
-  if (p.drop_on) return launch_fwd16_s<T, false, true>(p, s);
-  return p.block_mask != nullptr ? launch_fwd16_s<T, true, false>(p, s) : launch_fwd16_s<T, false, false>(p, s);
-}
-
+// d = 128 is instantiated in fa_fwd16_d128.hip, a unit compiled with other
+// scheduling; this unit holds d = 64 and the split-key merge.
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s) {
-  return p.dtype == 1 ? launch_fwd16_d<_Float16>(p, s) : launch_fwd16_d<__bf16>(p, s);
+  if (p.splits > 1 && p.Nq == 1) return launch_decode(p, s);  // one query row per head
+  if (p.d == 128) return launch_fwd16_128(p, s);
+  return p.dtype == 1 ? launch_fwd16_dd<_Float16, 64>(p, s) : launch_fwd16_dd<__bf16, 64>(p, s);
 }
+#else
+hipError_t launch_fwd16_128(const FwdProblem& p, hipStream_t s) {
+  return p.dtype == 1 ? launch_fwd16_dd<_Float16, 128>(p, s) : launch_fwd16_dd<__bf16, 128>(p, s);
+}
+#endif
 
 }  // namespace fa

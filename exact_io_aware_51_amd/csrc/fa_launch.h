@@ -63,6 +63,7 @@ struct BwdProblem {
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s);  // bf16 / fp16 only
+hipError_t launch_fwd16_128(const FwdProblem& p, hipStream_t s);  // d = 128 (fa_fwd16_d128.hip)
 hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s);   // E4M3 q, k, v; bf16 o; Nq = Nk, dense
 // split keys (p.splits > 1, 16-bit): partials into p.part, then the merge into o / lse
 hipError_t launch_decode(const FwdProblem& p, hipStream_t s);       // Nq == 1
