@@ -526,8 +526,6 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
 #endif
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   if constexpr (!SPARSE) {
     if (first < nt) {
       fetch(first, 0);
@@ -543,26 +541,29 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
     }
   } else {
     // Only live query tiles are visited, in increasing order, alternating
-    // stages; a step is unmasked when its tile lies in [full0, full1).
+    // stages; a step is unmasked when its tile lies in [full0, full1).  As in
+    // the dense loops, the stage is a runtime value and masked and unmasked
+    // tiles run in loops of their own (one loop holding both step bodies
+    // made the compiler shuffle the accumulators between register sets).
     auto next = [&](int i) __attribute__((always_inline)) { return next_live_tile(mwords, i, 2, a.nbq, nt); };
-    auto visit = [&](int i, int in, auto st) __attribute__((always_inline)) {
-      if (full0 <= i && i < full1)
-        step(i, in, st, std::true_type{});
-      else
-        step(i, in, st, std::false_type{});
-    };
     int i = live_tile_from(mwords, first, 2, a.nbq, nt);
     if (i < nt) {
       fetch(i, 0);
-      while (true) {
-        int in = next(i);
-        visit(i, in, I0{});
+      int st = 0;
+      for (; i < nt && i < full0; st ^= 1) {
+        const int in = next(i);
+        step(i, in, st, std::false_type{});
         i = in;
-        if (i >= nt) break;
-        in = next(i);
-        visit(i, in, I1{});
+      }
+      for (; i < full1; st ^= 1) {
+        const int in = next(i);
+        step(i, in, st, std::true_type{});
         i = in;
-        if (i >= nt) break;
+      }
+      for (; i < nt; st ^= 1) {
+        const int in = next(i);
+        step(i, in, st, std::false_type{});
+        i = in;
       }
     }
   }
