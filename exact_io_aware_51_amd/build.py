@@ -30,12 +30,14 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function"]
 # Per-source flags.  The backward kernels and the d = 128 forward are
 # scheduled with LLVM's max-ILP strategy: measured on MI355X, dQ +2.5% and
-# dK/dV +2.5% on the c5 backward, d = 64 dK/dV +2.4%, the c5 forward +3.9%.
+# dK/dV +2.5% on the c5 backward, d = 64 dK/dV +2.4%, the c5 forward +3.9%,
+# the E4M3 forward +2.0% (c4 shape) and +2.4% (c3 shape).
 # The dropout backward (17% slower under it) and the d = 64 forward (4%
 # slower) keep the default: fa_bwd16_drop.hip and fa_fwd16_d128.hip compile
 # those parts of fa_bwd16.hip / fa_fwd16.hip as units of their own.
 SOURCE_FLAGS = {"fa_bwd16.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-                "fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+                "fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                "fa_fwd8.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:

@@ -298,12 +298,17 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
       step(j, jn, -1, 0, 0, std::false_type{});
       int jp = j, t = 1;
       j = jn;
+      // unmasked tiles (below nt_full) come first in the walk: two loops, so
+      // that no loop holds both step bodies
+      for (; j < nt_full; ++t) {
+        jn = next(j);
+        step(j, jn, jp, t % 3, t & 1, std::true_type{});
+        jp = j;
+        j = jn;
+      }
       for (; j < nt; ++t) {
         jn = next(j);
-        if (j < nt_full)
-          step(j, jn, jp, t % 3, t & 1, std::true_type{});
-        else
-          step(j, jn, jp, t % 3, t & 1, std::false_type{});
+        step(j, jn, jp, t % 3, t & 1, std::false_type{});
         jp = j;
         j = jn;
       }
