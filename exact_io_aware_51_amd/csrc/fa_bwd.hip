@@ -1,4 +1,6 @@
-// fa_bwd.hip -- backward pass of fused exact attention for gfx950.
+// fa_bwd.hip -- backward pass of fused exact attention for gfx950: the row
+// sums D for every dtype, dK/dV and dQ for fp32 I/O (16-bit I/O runs the
+// kernels of fa_bwd16.hip).
 //
 // Only O and the per-row log-sum-exp were kept by the forward pass; the score
 // tiles are recomputed here tile by tile from Q, K and LSE, never read from
@@ -461,17 +463,34 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// Row sums D (every dtype and head size).
+template <typename T, int D>
+static hipError_t launch_pre_t(const BwdProblem& p, hipStream_t stream) {
+  const long long rows = (long long)p.B * p.H * p.Nq;
+  constexpr int LPR = D / (16 / sizeof(T));
+  constexpr int RPB = 256 / LPR;
+  const long long blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const T*>(p.o), reinterpret_cast<const T*>(p.dout), p.dvec, rows);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_pre_d(const BwdProblem& p, hipStream_t s) {
+  return p.d == 64 ? launch_pre_t<T, 64>(p, s) : launch_pre_t<T, 128>(p, s);
+}
+
+static hipError_t launch_pre(const BwdProblem& p, hipStream_t s) {
+  switch (p.dtype) {
+    case 0: return launch_pre_d<float>(p, s);
+    case 1: return launch_pre_d<_Float16>(p, s);
+    default: return launch_pre_d<__bf16>(p, s);
+  }
+}
+
+// dK/dV (stage 1) or dQ (stage 2) for fp32 I/O.
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_bwd_t(const BwdProblem& p, int stage, hipStream_t stream) {
-  if (stage == 0) {
-    const long long rows = (long long)p.B * p.H * p.Nq;
-    constexpr int LPR = D / (16 / sizeof(T));
-    constexpr int RPB = 256 / LPR;
-    const long long blocks = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const T*>(p.o), reinterpret_cast<const T*>(p.dout), p.dvec, rows);
-    return hipGetLastError();
-  }
   BwdArgs a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.dout = p.dout; a.lse = p.lse;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv; a.dvec = p.dvec;
@@ -501,28 +520,15 @@ static hipError_t launch_bwd_s(const BwdProblem& p, int stage, hipStream_t s) {
                   : launch_bwd_t<T, 128, false, SPARSE, DROP>(p, stage, s);
 }
 
-// (block sparsity and dropout are not combined: the API rejects that)
-template <typename T>
-static hipError_t launch_bwd_d(const BwdProblem& p, int stage, hipStream_t s) {
-  if (p.drop_on) return launch_bwd_s<T, false, true>(p, stage, s);
-  return p.block_mask != nullptr ? launch_bwd_s<T, true, false>(p, stage, s) : launch_bwd_s<T, false, false>(p, stage, s);
-}
-
-#ifndef FA_DQ16
-#define FA_DQ16 1
-#endif
-#ifndef FA_DKDV16
-#define FA_DKDV16 1
-#endif
-
+// The dK/dV and dQ kernels above serve fp32 I/O; 16-bit I/O runs the kernels
+// of fa_bwd16.hip.  (Block sparsity and dropout are not combined: the API
+// rejects that.)
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s) {
-  if (stage == 2 && p.dtype != 0 && FA_DQ16) return launch_dq16(p, s);
-  if (stage == 1 && p.dtype != 0 && FA_DKDV16) return launch_dkdv16(p, s);
-  switch (p.dtype) {
-    case 0: return launch_bwd_d<float>(p, stage, s);
-    case 1: return launch_bwd_d<_Float16>(p, stage, s);
-    default: return launch_bwd_d<__bf16>(p, stage, s);
-  }
+  if (stage == 0) return launch_pre(p, s);
+  if (p.dtype != 0) return stage == 1 ? launch_dkdv16(p, s) : launch_dq16(p, s);
+  if (p.drop_on) return launch_bwd_s<float, false, true>(p, stage, s);
+  return p.block_mask != nullptr ? launch_bwd_s<float, true, false>(p, stage, s)
+                                 : launch_bwd_s<float, false, false>(p, stage, s);
 }
 
 }  // namespace fa

@@ -41,12 +41,9 @@ struct Bwd16Args {
   float scale;
 };
 
-#ifndef FA_BWD_TR_AHEAD
-#define FA_BWD_TR_AHEAD 0
-#endif
-#ifndef FA_BWD_READAHEAD
-#define FA_BWD_READAHEAD 12
-#endif
+// Row-fragment reads kept in flight ahead of the S / dP products of the
+// one-wave kernels (all twelve of a 32-row half at d = 128).
+constexpr int kBwdReadAhead = 12;
 
 // Scheduling hint: NM matrix ops with R LDS reads each, the reads issued P
 // matrix ops ahead of their use.
@@ -61,10 +58,6 @@ __device__ inline void reads_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
 }
 
-#ifndef FA_DQ_PRIO
-#define FA_DQ_PRIO 1
-#endif
-
 // --------------------------------------------------------------------------
 // dQ: a workgroup owns 128 queries (32 per wave, Q and dO rows in VGPRs) and
 // streams 64-key K/V tiles.  Step j computes S^T_j = K_j Q^T and
@@ -76,17 +69,11 @@ __device__ inline void reads_ahead() {
 // extra read-ahead schedule.  Carrying dS into the next step (the schedule of
 // d = 64 and of the dropout / block-sparse kernels) needs ~300 VGPRs and so
 // one wave per SIMD, which measured 9% slower on the c5 backward.
-#ifndef FA_DQ_TWO_WAVES
-#define FA_DQ_TWO_WAVES 1
-#endif
-#ifndef FA_DQ_READAHEAD
-#define FA_DQ_READAHEAD 0
-#endif
 template <int D, bool SPARSE, bool DROP>
 struct DqShape {
-  static constexpr bool TWO = FA_DQ_TWO_WAVES && D == 128 && !SPARSE && !DROP;
+  static constexpr bool TWO = D == 128 && !SPARSE && !DROP;
   static constexpr int OCC = D == 64 || TWO ? 2 : 1;
-  static constexpr int AHEAD = TWO ? FA_DQ_READAHEAD : FA_BWD_READAHEAD;
+  static constexpr int AHEAD = TWO ? 0 : kBwdReadAhead;
 };
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
@@ -182,9 +169,6 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
         for (int mb = 0; mb < MB; ++mb)
           dqacc[mb] = M::mma(tile16_tr_frag<T, D>(smem, ktr[mb][0], ktr[mb][1], kps * TL::BYTES + (32 * kb + 16 * t) * TL::ROWB),
                              dsf[kb][t], dqacc[mb]);
-#if FA_BWD_TR_AHEAD
-    reads_ahead<4 * MB, 2, FA_BWD_TR_AHEAD>();
-#endif
   };
 
   // Step j (jp: the tile visited before it, jn: the one after; j - 1 and j + 1
@@ -208,9 +192,7 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
       // the two 32-key halves one after the other keeps two accumulators live, not four
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#if FA_DQ_PRIO
         __builtin_amdgcn_s_setprio(1);
-#endif
         f32x16 s = f32x16{}, p = f32x16{};
         const int ko = ks3 * TL::BYTES + kb * 32 * TL::ROWB, vo = vs2 * TL::BYTES + kb * 32 * TL::ROWB;
 #pragma unroll
@@ -219,9 +201,7 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
           p = M::mma(tile16_row_frag<T>(smem, vrow[ks] + vo), dof[ks], p);
         }
         if constexpr (AHEAD > 0) reads_ahead<2 * KSTEPS, 1, (AHEAD > 0 ? AHEAD : 1)>();
-#if FA_DQ_PRIO
         __builtin_amdgcn_s_setprio(0);
-#endif
         if (!NOPIPE && kb == 0 && prev) dq_prev(kps);
         const int tk = t0 - 32 * kb;
         // dropout: dP of a dropped weight is 0, of a kept one dP / (1 - p)
@@ -347,12 +327,8 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
 // d = 64 (no dropout): the kernel fits 256 VGPRs without spills, so two waves
 // share each SIMD; measured 1.5x faster than one.  d = 128 needs ~450 and the
 // dropout instantiations spill at 256: one wave.
-#ifndef FA_DKDV_OCC64
-#define FA_DKDV_OCC64 2
-#endif
-
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void dkdv16_kernel(Bwd16Args a) {
+__global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel(Bwd16Args a) {
   using M = Mma<T>;
   using TL = Tile16<D>;
   using Frag = typename M::Frag;
@@ -372,7 +348,7 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
   const int Nq = a.Nq, Nk = a.Nk;
 
   int bh, kblk;  // under the causal mask key block 0 is seen by the most query tiles
-  block_order<((D == 64 && !DROP) ? 32 * FA_DKDV_OCC64 : 32)>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
+  block_order<((D == 64 && !DROP) ? 64 : 32)>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
   const int kb0 = kblk * 128;
   const int kw = kb0 + 32 * wave;
   const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
@@ -479,9 +455,7 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
         s = M::mma(tile16_row_frag<T>(smem, qrow[ks] + qo + 32 * qb * TL::ROWB), kf[ks], s);
         dp = M::mma(tile16_row_frag<T>(smem, qrow[ks] + oo + 32 * qb * TL::ROWB), vf[ks], dp);
       }
-#if FA_BWD_READAHEAD
-      reads_ahead<2 * KSTEPS, 1, FA_BWD_READAHEAD>();
-#endif
+      reads_ahead<2 * KSTEPS, 1, kBwdReadAhead>();
       // rows of s / dp: queries i0 + 32 qb + acc_row(r, h); column: key mykey
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -526,9 +500,6 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? FA_DKDV_OCC64 : 1) void d
           dvacc[mb] = M::mma(tile16_tr_frag<T, D>(smem, qtr[mb][0] + oo, qtr[mb][1] + oo, off), pf[qb][t], dvacc[mb]);
           dkacc[mb] = M::mma(tile16_tr_frag<T, D>(smem, qtr[mb][0] + qo, qtr[mb][1] + qo, off), sf[qb][t], dkacc[mb]);
         }
-#if FA_BWD_TR_AHEAD
-    reads_ahead<8 * MB, 2, FA_BWD_TR_AHEAD>();
-#endif
   };
 
   if constexpr (!SPARSE) {

@@ -52,16 +52,12 @@ template <> struct Half2<_Float16> {
   __device__ static inline float hi(uint32_t x) { return (float)__builtin_bit_cast(V, x)[1]; }
 };
 
-#ifndef FA_DECODE_UNROLL
-#define FA_DECODE_UNROLL 4
-#endif
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   using P = Half2<T>;
   constexpr int LPK = D / 8;       // lanes per key row (8 channels, 16 bytes each)
   constexpr int KPI = 64 / LPK;    // keys per load instruction: 4 (d = 128) or 8 (d = 64)
-  constexpr int U = FA_DECODE_UNROLL;  // key slots per lane and iteration
+  constexpr int U = 4;  // key slots per lane and iteration
   constexpr int STEP = U * KPI;    // keys per wave and iteration
   __shared__ float red[4][D + 2];
 

@@ -1,4 +1,5 @@
-// fa_fwd.hip -- fused exact-attention forward pass for gfx950.
+// fa_fwd.hip -- fused exact-attention forward pass for fp32 I/O on gfx950
+// (16-bit I/O runs the pipelined kernels of fa_fwd16.hip).
 //
 // One workgroup owns a block of BM = 128 query rows of one (batch, head) and
 // streams the key/value tiles of that head past it ("How Flash Attention
@@ -68,26 +69,6 @@ struct FwdLayout {
 // against the same reference, so the final O = acc / l is unchanged; the
 // weights 2^(c s - m) stay below 2^kTau, far inside fp32 and bf16 range.
 constexpr float kTau = 8.0f;
-
-#ifndef FA_FWD_SCHED
-#define FA_FWD_SCHED 0
-#endif
-#ifndef FA_FWD_PVORDER
-#define FA_FWD_PVORDER 0
-#endif
-
-// Ask the scheduler to interleave NM matrix ops with their LDS reads
-// (R reads per op), keeping the reads P ops ahead.
-template <int NM, int R, int P>
-__device__ inline void interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, R * P, 0);
-#pragma unroll
-  for (int i = 0; i < NM - P; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
-}
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) void fwd_kernel(FwdArgs a) {
@@ -195,9 +176,6 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
       s0 = M::mma(row_frag<T>(kr0 + ks * M::KS, h), qf[ks], s0);
       s1 = M::mma(row_frag<T>(kr1 + ks * M::KS, h), qf[ks], s1);
     }
-#if FA_FWD_SCHED
-    interleave<2 * KSTEPS, 1, 4>();
-#endif
     // key of register r in block kb is k0 + 32 kb + acc_row(r, h); allowed iff <= lim
     const int t0 = lim - k0 - 4 * h, t1 = t0 - 32;
     float mx = -__builtin_inff();
@@ -254,24 +232,12 @@ __global__ __launch_bounds__(kFwdThreads, (sizeof(T) == 2 || D == 64) ? 2 : 1) v
     for (int t = 0; t < PSTEPS; ++t) {
       const Frag pf0 = acc_frag<T>(s0, t);
       const Frag pf1 = acc_frag<T>(s1, t);
-#if FA_FWD_PVORDER
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 0, t, 32 * mb, lane), pf0, oacc[mb]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 32, t, 32 * mb, lane), pf1, oacc[mb]);
-#else
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 0, t, 32 * mb, lane), pf0, oacc[mb]);
         oacc[mb] = M::mma(trans_frag<T>(vt, L::VSTR, 32, t, 32 * mb, lane), pf1, oacc[mb]);
       }
-#endif
     }
-#if FA_FWD_SCHED
-    interleave<2 * PSTEPS * MB, (sizeof(T) == 2 ? 2 : 1), 2>();
-#endif
   };
 
   if (ntiles > 0) {
@@ -349,21 +315,13 @@ static hipError_t launch_fwd_s(const FwdProblem& p, hipStream_t s) {
   return p.causal ? launch_fwd_t<T, 128, true, SPARSE, DROP>(p, s) : launch_fwd_t<T, 128, false, SPARSE, DROP>(p, s);
 }
 
-// (block sparsity and dropout are not combined: the API rejects that)
-template <typename T>
-static hipError_t launch_fwd_d(const FwdProblem& p, hipStream_t s) {
-  if (p.drop_on) return launch_fwd_s<T, false, true>(p, s);
-  return p.block_mask != nullptr ? launch_fwd_s<T, true, false>(p, s) : launch_fwd_s<T, false, false>(p, s);
-}
-
-#ifndef FA_FWD16
-#define FA_FWD16 1
-#endif
-
+// fp32 I/O runs this kernel; 16-bit I/O runs the pipelined kernels of
+// fa_fwd16.hip.  (Block sparsity and dropout are not combined: the API
+// rejects that.)
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s) {
-  if (p.dtype == 0) return launch_fwd_d<float>(p, s);
-  if (FA_FWD16) return launch_fwd16(p, s);
-  return p.dtype == 1 ? launch_fwd_d<_Float16>(p, s) : launch_fwd_d<__bf16>(p, s);
+  if (p.dtype != 0) return launch_fwd16(p, s);
+  if (p.drop_on) return launch_fwd_s<float, false, true>(p, s);
+  return p.block_mask != nullptr ? launch_fwd_s<float, true, false>(p, s) : launch_fwd_s<float, false, false>(p, s);
 }
 
 }  // namespace fa

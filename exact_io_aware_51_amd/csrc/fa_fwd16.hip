@@ -59,23 +59,13 @@ struct Fwd16Args {
   float* part_lse;
 };
 
-#ifndef FA16_PRIO
-#define FA16_PRIO 1
-#endif
-#ifndef FA16_SPEC
-#define FA16_SPEC 1
-#endif
-#ifndef FA16_SCHED
-#define FA16_SCHED 4
-#endif
-
-#ifndef FA_FWD_BN64
-#define FA_FWD_BN64 64
-#endif
+// K-fragment reads kept in flight ahead of the score products (measured: 4
+// and 8 within 1%, 12 slower)
+constexpr int kFwdReadAhead = 4;
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP, bool SPLIT = false>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
-  constexpr int BN = D == 64 ? FA_FWD_BN64 : 64;  // keys per tile
+  constexpr int BN = 64;  // keys per tile
   constexpr int KB = BN / 32;                      // 32-key blocks per tile
   using M = Mma<T>;
   using TL = Tile16<D, BN>;
@@ -225,7 +215,6 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
     const bool act = NOMASK || !CAUSAL || k0 <= wlast;
     const bool prev = FULL || (jp >= 0 && (!CAUSAL || BN * jp <= wlast));
     if (act) {
-#if FA16_PRIO
       // Wave priority: low for the score products, raised again for the
       // element-wise phase.  The two waves of a SIMD alternate between these
       // phases; the products are long and independent (one issue per 32
@@ -233,7 +222,6 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
       // dependent VALU instructions whose issue delays stall its wave.
       // Measured against the opposite assignment: c4 +4.5%, c5 +5.7%.
       __builtin_amdgcn_s_setprio(0);
-#endif
       f32x16 sc[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{};
@@ -241,20 +229,15 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
       for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) sc[kb] = M::mma(kfrag(KST, kb, ks), qf[ks], sc[kb]);
-#if FA16_SCHED
-      // keep FA16_SCHED K-fragment reads in flight ahead of the matrix ops
-      __builtin_amdgcn_sched_group_barrier(0x100, FA16_SCHED, 0);
+      // keep kFwdReadAhead K-fragment reads in flight ahead of the matrix ops
+      __builtin_amdgcn_sched_group_barrier(0x100, kFwdReadAhead, 0);
 #pragma unroll
-      for (int i = 0; i < KB * KSTEPS - FA16_SCHED; ++i) {
+      for (int i = 0; i < KB * KSTEPS - kFwdReadAhead; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, FA16_SCHED, 0);
-#endif
-#if FA16_PRIO
+      __builtin_amdgcn_sched_group_barrier(0x008, kFwdReadAhead, 0);
       __builtin_amdgcn_s_setprio(1);
-#endif
-#if FA16_SPEC
       if constexpr (FULL) {
         // Unmasked tile: exponentiate against the running maximum m without
         // looking for this tile's maximum first. If a lane's partial row sum
@@ -305,7 +288,6 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(Fwd16Args a) {
         l += rs;
         return;
       }
-#endif
       // key of register r in block kb is k0 + 32 kb + acc_row(r, h); allowed iff <= lim
       const int t0 = lim - k0 - 4 * h;
       float xs[KB * 16];
