@@ -210,6 +210,40 @@ def _check(*ts):
             raise ValueError("tensors must be contiguous [B, H, N, d]")
 
 
+def _check_like(t, ref, what):
+    """t must be a contiguous tensor with ref's shape, dtype and device."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device != ref.device or t.dtype != ref.dtype:
+        raise ValueError(f"{what} must be a {ref.dtype} tensor on {ref.device}")
+    if tuple(t.shape) != tuple(ref.shape) or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous with shape {tuple(ref.shape)}")
+    return t
+
+
+def _check_rows(t, shape, device, what):
+    """t must be a contiguous float32 tensor of `shape` on `device` (LSE and row vectors)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device != device or t.dtype != torch.float32:
+        raise ValueError(f"{what} must be a float32 tensor on {device}")
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous with shape {tuple(shape)}")
+    return t
+
+
+def _workspace(workspace, need, device):
+    """A caller's workspace (checked: device, contiguous, large enough) or a new one; returns (tensor, bytes)."""
+    import torch
+    if workspace is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        return ws, ws.numel()
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, {need} needed")
+    return workspace, nbytes
+
+
 def _stream(t, stream):
     import torch
     if stream is not None:
@@ -223,8 +257,10 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, need_lse=True
     _check(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    if need_lse and lse is None:
+    o = torch.empty_like(q) if out is None else _check_like(out, q, "out")
+    if lse is not None:
+        _check_rows(lse, (B, H, N), q.device, "lse")
+    elif need_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                 lse.data_ptr() if lse is not None else None, B, H, N, d, scale, int(bool(causal)),
@@ -241,12 +277,11 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, workspace=None, st
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_bytes(B, H, N, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_rows(lse, (B, H, N), q.device, "lse")
+    workspace, wsb = _workspace(workspace, fa_bwd_workspace_bytes(B, H, N, d, code), q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), wsb,
                 B, H, N, d, scale, int(bool(causal)), code, _stream(q, stream))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
@@ -309,8 +344,8 @@ def backward_kv(q, k, v, o, lse, dout, seqlens_q=None, seqlens_k=None, scale=Non
     sq, sk = _lengths(seqlens_q, B, q.device), _lengths(seqlens_k, B, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_bytes(B, H, Nq, d, code)
-    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_rows(lse, (B, H, Nq), q.device, "lse")
+    workspace, _ = _workspace(None, fa_bwd_workspace_bytes(B, H, Nq, d, code), q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -356,8 +391,8 @@ def backward_sparse(q, k, v, o, lse, dout, block_mask, scale=None, causal=False,
     m = _block_mask(block_mask, B, H, N, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_bytes(B, H, N, d, code)
-    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_rows(lse, (B, H, N), q.device, "lse")
+    workspace, _ = _workspace(None, fa_bwd_workspace_bytes(B, H, N, d, code), q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),
@@ -390,8 +425,8 @@ def backward_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, scale=Non
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    need = fa_bwd_workspace_bytes(B, H, N, d, code)
-    workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_rows(lse, (B, H, N), q.device, "lse")
+    workspace, _ = _workspace(None, fa_bwd_workspace_bytes(B, H, N, d, code), q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(),

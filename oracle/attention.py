@@ -115,15 +115,39 @@ def attention_forward_rows(q, k, v, scale, causal, b, h, rows):
     return o, lse
 
 
-def _backward_head(q, k, v, do, scale, causal):
+def attention_forward_panel(q, k, v, scale, causal, b, h, r0, r1):
+    """O and LSE for the contiguous query rows r0 .. r1-1 of one (b, h) slice.
+
+    The same definition as attention_forward on whole rows (rows never
+    interact), for checking long sequences a panel at a time.
+    """
+    qh, kh, vh = _f64(q[b, h, r0:r1]), _f64(k[b, h]), _f64(v[b, h])
+    p, lse = _softmax_rows(_scores(qh, kh, scale, causal, row0=r0))
+    return p @ vh, lse
+
+
+def _backward_terms(q, k, v, do, scale, causal):
+    """P, dP = dO V^T, D_i = sum_j P_ij dP_ij and dS = P * (dP - D) for one head."""
     p, _ = _softmax_rows(_scores(q, k, scale, causal))
-    dv = p.T @ do
     dp = do @ v.T
     dsum = np.sum(p * dp, axis=1, keepdims=True)
     ds = p * (dp - dsum)
+    return p, dp, dsum[:, 0], ds
+
+
+def _backward_head(q, k, v, do, scale, causal):
+    p, _, _, ds = _backward_terms(q, k, v, do, scale, causal)
+    dv = p.T @ do
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     return dq, dk, dv
+
+
+def attention_backward_terms(q, k, v, do, scale, causal, b, h):
+    """The intermediate matrices of one (b, h) slice's backward pass:
+    (P, dP, D, dS), each N x N except D (length N).  For error models of
+    implementations that round P or dS before multiplying."""
+    return _backward_terms(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h]), scale, causal)
 
 
 def attention_backward(q, k, v, do, scale, causal, heads=None):

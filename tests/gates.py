@@ -49,3 +49,84 @@ def check_lse(x, ref, dtype, what):
     assert np.all(np.isfinite(x)), f"{what}: non-finite LSE"
     assert err <= LSE_ABS[dtype], f"{what}: LSE max abs err {err:.3e} > {LSE_ABS[dtype]:.0e}"
     return err
+
+
+def check_blocks(x, ref, dtype, what, rel_gate=None, block=128):
+    """check() over a whole [B, H, N, d] tensor, also per (b, h) head: the
+    relative Frobenius gate holds for every head on its own, and a failure
+    names the (b, h, 128-row block) where the worst element sits."""
+    x, ref = to_np(x), to_np(ref)
+    assert x.shape == ref.shape, f"{what}: shape {x.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(x)), f"{what}: non-finite values at {np.argwhere(~np.isfinite(x))[0].tolist()}"
+    diff = np.abs(x - ref)
+    if dtype == "f32":
+        excess = diff - 1e-4
+    else:
+        excess = diff - (2e-2 + 1e-2 * np.abs(ref))
+    b, h, i, c = np.unravel_index(int(np.argmax(excess)), excess.shape)
+    assert excess[b, h, i, c] <= 0.0, (f"{what}: gate exceeded by {excess[b, h, i, c]:.3e} at head ({b}, {h}), "
+                                       f"row {i} (block {i // block}), column {c}")
+    gate = rel_gate if rel_gate is not None else FWD_REL[dtype]
+    num = np.sqrt(np.sum((x - ref) ** 2, axis=(2, 3)))
+    den = np.sqrt(np.sum(ref ** 2, axis=(2, 3)))
+    rel = num / np.where(den > 0, den, 1.0)
+    b, h = np.unravel_index(int(np.argmax(rel)), rel.shape)
+    assert rel[b, h] <= gate, f"{what}: relative Frobenius error {rel[b, h]:.3e} > {gate:.1e} in head ({b}, {h})"
+    return {"max_abs": float(diff.max()), "rel_fro_worst_head": float(rel.max())}
+
+
+def check_lse_blocks(x, ref, dtype, what, block=128):
+    """check_lse() over [B, H, N], naming the (b, h, 128-row block) of the worst row."""
+    x, ref = to_np(x), to_np(ref)
+    assert np.all(np.isfinite(x)), f"{what}: non-finite LSE"
+    err = np.abs(x - ref)
+    b, h, i = np.unravel_index(int(np.argmax(err)), err.shape)
+    assert err[b, h, i] <= LSE_ABS[dtype], (f"{what}: LSE max abs err {err[b, h, i]:.3e} > {LSE_ABS[dtype]:.0e} at "
+                                            f"head ({b}, {h}), row {i} (block {i // block})")
+    return float(err.max())
+
+
+# Unit roundoff u and half the smallest subnormal spacing eta of the 16-bit I/O types:
+# a rounded value x' satisfies |x' - x| <= u |x| + eta.
+ROUNDING = {"bf16": (2.0 ** -8, 2.0 ** -134), "f16": (2.0 ** -11, 2.0 ** -25)}
+
+
+def bwd_rounding_bound(q, k, v, do, o, terms, scale, dtype):
+    """First-order bound on the gradient error of a 16-bit backward pass that
+    follows the recompute scheme, for one head ([N, d] float64 q, k, v, do,
+    the exact output o, and terms = (P, dP, D, dS) from the oracle).
+
+    Roundings to the I/O type (unit roundoff u, subnormal half-spacing eta):
+      * the forward rounds P before P V and rounds O at the store, and
+        D_i = sum_c dO_ic O_ic is formed from that O;
+      * P is rounded before dV = P^T dO, and dS = P (dP - D) before
+        dQ = scale dS K and dK = scale dS^T Q;
+      * dQ, dK, dV are rounded once more at the store.
+    fp32 work, with worst-case accumulation factors g_n = n 2^-24: the scores
+    (d products, error g_d sum_c |q_ic k_jc| before the scale), the
+    exponentials (2^-22 relative), the log-sum-exp (the scores' error plus the
+    forward's sum of N weights), dP (g_d sum_c |dO_ic v_jc|), D, and every
+    sum of N products.  Returns bounds shaped like (dQ, dK, dV)."""
+    u, eta = ROUNDING[dtype]
+    n, d = q.shape[0], q.shape[1]
+    g_d, g_n = d * 2.0 ** -24, n * 2.0 ** -24
+    p, dp, dd, ds = terms
+    aq, ak, av, ado = np.abs(q), np.abs(k), np.abs(v), np.abs(do)
+    a_s = aq @ ak.T                                      # sum_c |q_ic k_jc|
+    sc = abs(scale)
+    # relative error of the fp32 weights exp(scale s_ij - LSE_i)
+    eps = sc * g_d * a_s + (sc * g_d * np.max(a_s, axis=1, keepdims=True) + g_n) + 2.0 ** -22
+    # forward output: P rounded and in error by eps, a sum of N products, O rounded
+    pv = p @ av
+    o_err = (u + g_n) * pv + (eps * p) @ av + eta * av.sum(axis=0)[None, :] + u * np.abs(o)
+    d_err = np.sum(ado * o_err, axis=1) + g_d * np.sum(ado * np.abs(o), axis=1)      # |D_gpu - D|
+    dp_err = g_d * (ado @ av.T)
+    e = (eps * p * np.abs(dp - dd[:, None]) + p * (dp_err + d_err[:, None])        # dS before rounding
+         + u * np.abs(ds) + eta)                                                     # and its rounding
+    gq = sc * (e @ ak + g_n * (np.abs(ds) @ ak))
+    gk = sc * (e.T @ aq + g_n * (np.abs(ds).T @ aq))
+    gv = ((u + eps + g_n) * p + eta).T @ ado
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    dv = p.T @ do
+    return (gq + u * np.abs(dq) + eta, gk + u * np.abs(dk) + eta, gv + u * np.abs(dv) + eta)

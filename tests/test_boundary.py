@@ -379,3 +379,31 @@ def test_python_helpers_refuse_cpu_tensors(fa):
     with pytest.raises(ValueError):
         fa.backward_kv(q, q, q, q, torch.zeros(1, 1, 4), q)
     assert math.isclose(1 / math.sqrt(64), 0.125)
+
+
+def test_python_helpers_check_caller_buffers(fa):
+    """Caller-supplied out / lse / workspace are checked before any launch: the
+    C ABI sees only addresses, so a wrong shape, dtype, device or an undersized
+    workspace would otherwise reach a kernel.  The checks are device-agnostic,
+    so CPU tensors stand in for device tensors here."""
+    import torch
+    q = torch.zeros(2, 3, 5, 64, dtype=torch.bfloat16)
+    assert fa._check_like(torch.empty_like(q), q, "out") is not None
+    for bad in (torch.empty(2, 3, 5, 64, dtype=torch.float16), torch.empty(2, 3, 6, 64, dtype=torch.bfloat16),
+                torch.empty(2, 3, 64, 5, dtype=torch.bfloat16).transpose(2, 3), "not a tensor"):
+        with pytest.raises(ValueError):
+            fa._check_like(bad, q, "out")
+    dev = q.device
+    assert fa._check_rows(torch.empty(2, 3, 5), (2, 3, 5), dev, "lse") is not None
+    for bad in (torch.empty(2, 3, 5, dtype=torch.bfloat16), torch.empty(2, 3, 4), torch.empty(2, 5, 3).transpose(1, 2),
+                torch.empty(30)):
+        with pytest.raises(ValueError):
+            fa._check_rows(bad, (2, 3, 5), dev, "lse")
+    ws, nb = fa._workspace(torch.empty(64, dtype=torch.float32), 256, dev)
+    assert nb == 256
+    with pytest.raises(ValueError):
+        fa._workspace(torch.empty(63, dtype=torch.float32), 256, dev)
+    with pytest.raises(ValueError):
+        fa._workspace(torch.empty(128, dtype=torch.float32)[::2], 256, dev)
+    ws, nb = fa._workspace(None, 1000, dev)
+    assert nb >= 1000 and ws.device == dev

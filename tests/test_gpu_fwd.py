@@ -38,42 +38,6 @@ def test_fwd_small_shapes(shape, causal, dtype):
     check_lse(lse, rl, dtype, f"LSE {w.name}")
 
 
-# ------------------------------------------------------- the five workloads
-def _sample_rows(N, rng, n=48):
-    rows = {0, 1, N // 2, N - 2, N - 1}
-    rows.update(rng.choice(N, size=min(N, n), replace=False).tolist())
-    return sorted(r for r in rows if 0 <= r < N)
-
-
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
-def test_fwd_workloads(name):
-    """Full-size launch; rows of a few heads checked against the oracle one by one."""
-    dev = device()
-    w = W.WORKLOADS[name]
-    announce("fwd workload", name)
-    q, k, v = W.make_inputs(w, with_grad=False)
-    o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, w.causal)
-    o_c, lse_c = o.cpu(), lse.cpu()
-    assert torch.isfinite(o_c.float()).all() and torch.isfinite(lse_c).all()
-    if w.N * w.B * w.H <= 4096:
-        ro, rl = oracle.attention_forward(q, k, v, w.scale, w.causal)
-        check(o_c, ro, w.dtype, f"O {name}")
-        check_lse(lse_c, rl, w.dtype, f"LSE {name}")
-        return
-    rng = np.random.default_rng(5)
-    heads = {(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))}
-    got, ref, gl, rlse = [], [], [], []
-    for (b, h) in sorted(heads):
-        rows = _sample_rows(w.N, rng)
-        so, sl = oracle.attention_forward_rows(q, k, v, w.scale, w.causal, b, h, rows)
-        got.append(to_np(o_c[b, h, rows]))
-        ref.append(so)
-        gl.append(to_np(lse_c[b, h, rows]))
-        rlse.append(sl)
-    check(np.concatenate(got), np.concatenate(ref), w.dtype, f"O rows {name}")
-    check_lse(np.concatenate(gl), np.concatenate(rlse), w.dtype, f"LSE rows {name}")
-
-
 # ----------------------------------------------------------- special cases
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_fwd_causal_row0_is_v0_exactly(dtype):
@@ -114,7 +78,12 @@ def test_fwd_unusual_scales(scale):
 
 
 def test_fwd_peaked_scores_are_stable():
-    """Large scores (peaked softmax rows) exercise the running-max rescaling."""
+    """Large scores (peaked softmax rows) exercise the running-max rescaling.
+
+    Inputs x4 put the scores 16x wider than the workloads'.  The LSE is fp32
+    work on exact 16-bit products, so the supplemental LSE gate applies
+    unchanged: its error is the fp32 rounding of sums of up to d products and
+    N weights, far below 1e-3 even at |LSE| ~ 100."""
     dev = device()
     w = W.shape_case(1, 2, 700, 128, "bf16", False, seed=8, mode="fwd", q_scale=4.0)
     announce("fwd peaked", w.name)
@@ -122,7 +91,7 @@ def test_fwd_peaked_scores_are_stable():
     o, lse = _fwd(*to_dev((q, k, v), dev), w.scale, False)
     ro, rl = oracle.attention_forward(q, k, v, w.scale, False)
     check(o, ro, "bf16", "O peaked")
-    assert np.max(np.abs(to_np(lse) - rl)) < 5e-3
+    check_lse(lse, rl, "bf16", "LSE peaked")
 
 
 def test_fwd_without_lse_and_determinism():
