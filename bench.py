@@ -148,10 +148,213 @@ def write_traffic(prof_dir, w):
     log(f"wrote {TRAFFIC_FILE} (factors {fetch_factor:.4f} / {write_factor:.4f})")
 
 
+# --------------------------------------------------------------- counter reports
+N_XCD, N_CU, MFMA_FLOP_PER_CU_CLK = 8, 256, 4096   # MI355X: 2.5 PFLOP/s dense bf16 = 256 CU x 2.4 GHz x 4096
+COUNTER_PASSES = [
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA "
+    "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_WAVES GRBM_GUI_ACTIVE",
+    "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY SQ_INSTS_VALU_TRANS_F32 "
+    "SQ_BUSY_CU_CYCLES SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+    "FETCH_SIZE",
+    "WRITE_SIZE",
+]
+WORKLOAD_CMDS = {  # the command each counter report profiles (from the repository root)
+    "c5": "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-fwd-workloads",
+    "c3": "python3 bench.py --fwd-workload c3 --steps 5 --warmup 2",
+    "c4": "python3 bench.py --fwd-workload c4 --steps 5 --warmup 2",
+}
+FWD_KERNELS = {"fwd16_kernel": "fwd", "fwd_kernel": "fwd"}
+
+
+def _pmc_per_kernel(run_dir):
+    """{kernel: {counter: mean per dispatch}} and {kernel: dispatches} from a --pmc run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (row["Kernel_Name"], row["Dispatch_Id"], row["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    acc, disp = {}, {}
+    for (kname, did, cname), v in per.items():
+        acc.setdefault(kname, {}).setdefault(cname, []).append(v)
+        disp.setdefault(kname, set()).add(did)
+    return ({k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()},
+            {k: len(v) for k, v in disp.items()})
+
+
+def _trace_stats(run_dir):
+    """{kernel: (calls, average ns, min ns)} from a --kernel-trace --stats run directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {run_dir}")
+    out = {}
+    with open(files[0], newline="") as f:
+        for row in csv.DictReader(f):
+            out[row["Name"]] = (int(row["Calls"]), float(row["AverageNs"]), float(row["MinNs"]))
+    return out
+
+
+def _stage_of(kname, w):
+    if w.mode == "fwd+bwd":
+        return next((v for k, v in STEP_KERNELS.items() if k in kname), None)
+    return next((v for k, v in FWD_KERNELS.items() if k in kname), None)
+
+
+def write_counter_report(prof_dir, w, cal_dir):
+    """profiles/<workload>_counters.{json,md} from rocprofv3 runs under prof_dir:
+    trace/ (--kernel-trace --stats) and pmc1 .. pmc4 (the COUNTER_PASSES of
+    WORKLOAD_CMDS[w.name]); cal_dir holds copy_FETCH_SIZE / copy_WRITE_SIZE
+    (bench.py --copy-calibration 1024) for the byte counters' scale."""
+    copy_bytes = 1024 << 20
+    cf, _ = _pmc_per_kernel(os.path.join(cal_dir, "copy_FETCH_SIZE"))
+    cw, _ = _pmc_per_kernel(os.path.join(cal_dir, "copy_WRITE_SIZE"))
+    cname = next(k for k in cf if "copyBuffer" in k)
+    ff = copy_bytes / (cf[cname]["FETCH_SIZE"] * 1024.0)
+    wf = copy_bytes / (cw[cname]["WRITE_SIZE"] * 1024.0)
+    trace = _trace_stats(os.path.join(prof_dir, "trace"))
+    ctr, calls = {}, {}
+    for i in range(1, len(COUNTER_PASSES) + 1):
+        c, n = _pmc_per_kernel(os.path.join(prof_dir, f"pmc{i}"))
+        for k, v in c.items():
+            ctr.setdefault(k, {}).update(v)
+            calls[k] = max(calls.get(k, 0), n[k])
+    models = kernel_models(w) if w.mode == "fwd+bwd" else {"fwd": kernel_models(w)["fwd"]}
+    e = 2 if w.dtype in ("bf16", "f16") else 4
+    bh, n_, d_ = w.B * w.H, w.N, w.d
+    naive_fwd = bh * (4.0 * n_ * n_ * e + 4.0 * n_ * d_ * e)  # write S, read S, write P, read P; Q, K, V, O once
+    rows = {}
+    for kname, c in ctr.items():
+        stage = _stage_of(kname, w)
+        if stage is None or stage not in models:
+            continue
+        m = models[stage]
+        tr = next((v for k, v in trace.items() if k == kname), None)
+        avg_ns = tr[1] if tr else None
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD          # cycles per XCD while the kernel ran
+        simd_cycles = gui * N_CU * 4
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        mfma_flops = 512.0 * mops
+        waves = c.get("SQ_WAVES", 0.0) or 1.0
+        hbm = c.get("FETCH_SIZE", 0.0) * 1024 * ff + c.get("WRITE_SIZE", 0.0) * 1024 * wf
+        r = {"kernel_symbol": kname, "dispatches_counted": calls[kname],
+             "trace_avg_us": round(avg_ns / 1e3, 2) if avg_ns else None,
+             "clock_mhz": round(gui / (avg_ns * 1e-9) / 1e6, 1) if avg_ns and gui else None,
+             "algorithmic_flops": m["flops"], "mfma_flops_executed": mfma_flops,
+             "mfma_flops_over_algorithmic": round(mfma_flops / m["flops"], 3) if m["flops"] else None,
+             "algorithmic_tflops_by_trace": round(m["flops"] / (avg_ns * 1e-9) / 1e12, 1) if avg_ns else None,
+             "frac_of_2p5_pflops_by_trace": round(m["flops"] / (avg_ns * 1e-9) / 2.5e15, 4) if avg_ns else None,
+             "mfma_util_at_measured_clock": round(mfma_flops / (MFMA_FLOP_PER_CU_CLK * N_CU * gui), 4) if gui else None,
+             "mfma_busy_per_simd": round(c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / simd_cycles, 4) if gui else None,
+             "mfma_valu_coexec_per_simd": round(c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / simd_cycles, 4) if gui else None,
+             "valu_active_per_simd": round(c.get("SQ_ACTIVE_INST_VALU", 0.0) / simd_cycles, 4) if gui else None,
+             "valu_insts_per_wave": round(c.get("SQ_INSTS_VALU", 0.0) / waves, 1),
+             "mfma_insts_per_wave": round(c.get("SQ_INSTS_MFMA", 0.0) / waves, 1),
+             "exp_insts_per_wave": round(c.get("SQ_INSTS_VALU_TRANS_F32", 0.0) / waves, 1),
+             "lds_insts_per_wave": round(c.get("SQ_INSTS_LDS", 0.0) / waves, 1),
+             "lds_bank_conflict_cycles": c.get("SQ_LDS_BANK_CONFLICT"),
+             "lds_bank_conflicts_per_lds_active_cycle": (round(c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"], 4)
+                                                         if c.get("SQ_ACTIVE_INST_LDS") else None),
+             "wait_lds_over_wait_any": (round(c.get("SQ_WAIT_INST_LDS", 0.0) / c["SQ_WAIT_INST_ANY"], 4)
+                                        if c.get("SQ_WAIT_INST_ANY") else None),
+             "waves": waves,
+             "hbm_bytes": int(hbm), "algorithmic_bytes": m["bytes"],
+             "hbm_over_algorithmic": round(hbm / m["bytes"], 3),
+             "hbm_gbs_by_trace": round(hbm / (avg_ns * 1e-9) / 1e9, 1) if avg_ns else None,
+             "raw_counters_per_dispatch": {k: round(v, 1) for k, v in sorted(c.items())}}
+        if stage == "fwd":
+            outs = bh * n_ * d_
+            r["bytes_per_output_element"] = round(hbm / outs, 2)
+            r["naive_4pass_bytes"] = naive_fwd
+            r["naive_bytes_per_output_element"] = round(naive_fwd / outs, 1)
+            r["naive_over_measured"] = round(naive_fwd / hbm, 1) if hbm else None
+        rows[stage] = r
+    cmd = WORKLOAD_CMDS[w.name]
+    rep = {"workload": f"{w.name}: {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} "
+                       f"{'causal' if w.causal else 'non-causal'} ({w.mode})",
+           "source_digest": source_digest(),
+           "commands": [f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace -o run -- {cmd}"] +
+                       [f"timeout -s KILL 90 rocprofv3 --pmc {p} --output-format csv -d DIR/pmc{i + 1} -o run -- {cmd}"
+                        for i, p in enumerate(COUNTER_PASSES)] +
+                       [f"timeout -s KILL 90 rocprofv3 --pmc {c} --output-format csv -d CAL/copy_{c} -o run -- "
+                        f"python3 bench.py --copy-calibration 1024" for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "calibration": {"copy_kernel": cname, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "kernels": rows}
+    base = os.path.join(ROOT, "profiles", f"{w.name}_counters")
+    with open(base + ".json", "w") as f:
+        json.dump(rep, f, indent=1)
+        f.write("\n")
+    with open(base + ".md", "w") as f:
+        f.write(_counter_markdown(rep))
+    log(f"wrote {base}.json / .md")
+    return rep
+
+
+def _counter_markdown(rep):
+    L = [f"# Counters: workload {rep['workload']}", "",
+         "Commands (from the repository root on the MI355X box, `cd /tmp && export TMPDIR=/tmp` first; DIR and "
+         "CAL are output folders):", "", "```"] + rep["commands"] + ["```", "",
+         f"Byte counters scaled by a 1 GiB device copy: FETCH_SIZE x {rep['calibration']['fetch_factor']}, "
+         f"WRITE_SIZE x {rep['calibration']['write_factor']}. `GRBM_GUI_ACTIVE` is summed over the 8 XCDs, so the "
+         "clock is its per-XCD value over the traced kernel time. MFMA utilisation counts "
+         "`SQ_INSTS_VALU_MFMA_MOPS_*` x 512 flops against 4096 flops per CU per clock at that clock; busy, "
+         "co-execution and VALU-active fractions are per SIMD (1024 SIMDs).", "",
+         f"Source digest of the kernels measured: `{rep['source_digest']}`.", ""]
+    keys = [("trace_avg_us", "trace avg (us)"), ("clock_mhz", "clock (MHz)"),
+            ("algorithmic_tflops_by_trace", "algorithmic TFLOP/s"), ("frac_of_2p5_pflops_by_trace", "of 2.5 PF"),
+            ("mfma_flops_over_algorithmic", "MFMA flops / algorithmic"),
+            ("mfma_util_at_measured_clock", "MFMA util at clock"), ("mfma_busy_per_simd", "MFMA busy / SIMD"),
+            ("mfma_valu_coexec_per_simd", "MFMA+VALU co-exec / SIMD"), ("valu_active_per_simd", "VALU active / SIMD"),
+            ("valu_insts_per_wave", "VALU insts / wave"), ("exp_insts_per_wave", "exp insts / wave"),
+            ("mfma_insts_per_wave", "MFMA insts / wave"), ("lds_insts_per_wave", "LDS insts / wave"),
+            ("lds_bank_conflicts_per_lds_active_cycle", "LDS bank conflict / LDS active"),
+            ("wait_lds_over_wait_any", "LDS wait / any wait"),
+            ("hbm_over_algorithmic", "HBM bytes / algorithmic"), ("hbm_gbs_by_trace", "HBM GB/s"),
+            ("bytes_per_output_element", "HBM bytes per output element"),
+            ("naive_bytes_per_output_element", "naive 4-pass bytes per output element"),
+            ("naive_over_measured", "naive / measured bytes")]
+    stages = list(rep["kernels"])
+    L.append("| metric | " + " | ".join(stages) + " |")
+    L.append("|---|" + "---|" * len(stages))
+    for k, label in keys:
+        vals = [rep["kernels"][s].get(k) for s in stages]
+        if all(v is None for v in vals):
+            continue
+        L.append(f"| {label} | " + " | ".join("" if v is None else str(v) for v in vals) + " |")
+    L.append("")
+    L.append("Kernel symbols: " + "; ".join(f"{s}: `{rep['kernels'][s]['kernel_symbol']}`" for s in stages))
+    L.append("")
+    return "\n".join(L)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, seconds):
-    """The fp64 oracle on whole heads of the same workload until `seconds` have passed."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
+    """The fp64 oracle on whole heads of the same workload, one (batch, head) per
+    host thread (one BLAS thread each), until `seconds` have passed.
+
+    Threads: the cores this process may run on (os.sched_getaffinity), at most
+    16, a GPU machine's CPU share per GPU.  numpy releases the interpreter lock in
+    its array loops and BLAS calls, so the heads run in parallel."""
+    import concurrent.futures
+
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     from exact_io_aware_51_amd import workloads as W
@@ -159,19 +362,39 @@ def cpu_baseline(w, seconds):
     models = kernel_models(w)
     per_head = sum(m["flops"] for m in models.values()) / (w.B * w.H)
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done, t0 = 0, time.perf_counter()
-    for (b, h) in heads:
+    host = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, host))
+    blas = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info() if p.get("user_api") == "blas"]
+
+    def one(bh):
+        b, h = bh
         sl = slice(b, b + 1), slice(h, h + 1)
         oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal)
         oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": per_head * done / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads of workload {w.name} (fwd+bwd per head, fp64 numpy, "
-                      f"{dt:.1f} s; algorithmic causal-adjusted flops)"}
+
+    done, t_end = 0, None
+    with threadpool_limits(limits=1, user_api="blas"):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            t0 = time.perf_counter()
+            todo = iter(heads)
+            running = {ex.submit(one, bh) for bh in [next(todo) for _ in range(min(workers, len(heads)))]}
+            while running:
+                fin, running = concurrent.futures.wait(running, return_when=concurrent.futures.FIRST_COMPLETED)
+                for f in fin:
+                    f.result()
+                    done += 1
+                t_end = time.perf_counter()
+                if t_end - t0 < seconds:
+                    for _ in fin:
+                        nxt = next(todo, None)
+                        if nxt is not None:
+                            running.add(ex.submit(one, nxt))
+    dt = t_end - t0
+    return {"value": per_head * done / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of workload {w.name} (fwd+bwd per head, fp64 numpy, one head "
+                      f"per thread, {dt:.1f} s; algorithmic causal-adjusted flops)",
+            "host_cores": host, "cpu_model": _cpu_model(), "blas": ", ".join(blas) or "unknown",
+            "blas_threads_per_worker": 1}
 
 
 class Runner:
@@ -357,7 +580,15 @@ def main():
                     help="diagnostic: run a plain device copy of MIB MiB five times (counter calibration)")
     ap.add_argument("--traffic-from", default=None, metavar="DIR",
                     help="write profiles/traffic.json from the rocprofv3 --pmc runs under DIR (no GPU needed)")
+    ap.add_argument("--counters-from", default=None, metavar="DIR",
+                    help="write profiles/<workload>_counters.{json,md} from the rocprofv3 runs under DIR "
+                         "(trace/, pmc1..pmc4; see WORKLOAD_CMDS) with --calibration-from CAL (no GPU needed)")
+    ap.add_argument("--calibration-from", default=None, metavar="CAL")
     args = ap.parse_args()
+    if args.counters_from:
+        from exact_io_aware_51_amd import workloads as W
+        write_counter_report(args.counters_from, W.WORKLOADS[args.workload], args.calibration_from)
+        return
     if args.traffic_from:
         from exact_io_aware_51_amd import workloads as W
         write_traffic(args.traffic_from, W.WORKLOADS[args.workload])
