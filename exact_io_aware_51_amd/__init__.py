@@ -22,11 +22,13 @@ __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd
            "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
            "backward_kv", "forward_sparse", "backward_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "forward_dropout", "backward_dropout", "fa_fwd_fp8", "forward_fp8", "fa_fwd_kv_split",
-           "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "SPARSE_BLOCK", "library_path", "load"]
+           "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "fa_bwd_static", "STATIC_SCRATCH_ROWS",
+           "SPARSE_BLOCK", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 SPARSE_BLOCK = 128  # rows and keys per block of a block-sparse mask (FA_SPARSE_BLOCK)
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
+STATIC_SCRATCH_ROWS = 1 << 22  # capacity of fa_bwd_static's device array (FA_STATIC_SCRATCH_ROWS)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -34,7 +36,7 @@ _LIB = None
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_fwd_fp8", "fa_fwd_kv_split", "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint",
-           "fa_status_string", "fa_version")
+           "fa_bwd_static", "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -63,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_static.restype = i
     lib.fa_bwd_rowsum.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
     lib.fa_bwd_rowsum.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, i, vp]
@@ -108,6 +112,10 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, 
            dtype, stream) -> int:
     return load().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d,
                          scale, causal, dtype, stream)
+
+
+def fa_bwd_static(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream) -> int:
+    return load().fa_bwd_static(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, stream)
 
 
 def fa_bwd_rowsum(o, dout, workspace, workspace_bytes, B, H, N, d, dtype, stream) -> int:

@@ -124,6 +124,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension or dtype (d must be 64 or 128; dtype fp32, fp16 or bf16)";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes()";
     case FA_ERR_HIP: return "the HIP runtime refused the launch (no device, invalid stream, or an earlier error)";
+    case FA_ERR_TOO_LARGE: return "B * H * N exceeds the static scratch of fa_bwd_static (FA_STATIC_SCRATCH_ROWS rows); use fa_bwd";
     default: return "unknown status";
   }
 }
@@ -256,7 +257,7 @@ int check_bwd(const BwdPtrs& p, size_t workspace_bytes, int B, int H, int Nq, in
   }
   if (p.lse != kUnused && (!p.lse || !aligned(p.lse, 4))) return FA_ERR_INVALID_ARG;
   const size_t need = fa_bwd_workspace_bytes(B, H, Nq, d, (fa_dtype)dtype);
-  if (!p.ws || workspace_bytes < need || !aligned(p.ws, 16)) return FA_ERR_WORKSPACE;
+  if (p.ws != kUnused && (!p.ws || workspace_bytes < need || !aligned(p.ws, 16))) return FA_ERR_WORKSPACE;
   const size_t tq = (size_t)B * H * Nq * d * elem_bytes(dtype);
   const size_t tk = (size_t)B * H * Nk * d * elem_bytes(dtype);
   const size_t lb = (size_t)B * H * Nq * sizeof(float);
@@ -283,7 +284,7 @@ fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d
   b.q = use(p.q); b.k = use(p.k); b.v = use(p.v); b.o = use(p.o); b.dout = use(p.dout);
   b.lse = static_cast<const float*>(use(p.lse));
   b.dq = const_cast<void*>(use(p.dq)); b.dk = const_cast<void*>(use(p.dk)); b.dv = const_cast<void*>(use(p.dv));
-  b.dvec = static_cast<float*>(p.ws);
+  b.dvec = static_cast<float*>(const_cast<void*>(use(p.ws)));
   b.B = B; b.H = H; b.Nq = Nq; b.Nk = Nk; b.d = d;
   b.seqlens_q = seqlens_q; b.seqlens_k = seqlens_k;
   b.block_mask = block_mask;
@@ -348,6 +349,21 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   if (st != FA_OK) return st;
   return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, drop), 0, 2,
                     stream);
+}
+
+int fa_bwd_static(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, fa_dtype dtype,
+                  void* stream) {
+  const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, const_cast<void*>(kUnused)};
+  int st = check_bwd(p, 0, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * N > fa::kStaticScratchRows) return FA_ERR_TOO_LARGE;
+  static_assert(fa::kStaticScratchRows == FA_STATIC_SCRATCH_ROWS, "fa.h states the scratch capacity");
+  float* dvec = nullptr;
+  if (fa::static_scratch(reinterpret_cast<hipStream_t>(stream), &dvec) != hipSuccess) return FA_ERR_HIP;
+  fa::BwdProblem b = bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
+  b.dvec = dvec;
+  return run_stages(b, 0, 2, stream);
 }
 
 int fa_bwd_rowsum(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B, int H, int N,

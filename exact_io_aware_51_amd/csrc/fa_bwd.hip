@@ -20,10 +20,52 @@
 // Every product keeps the owned rows as the accumulator's lane column, feeds
 // the recomputed P or dS back from registers as a B operand, and reads the
 // other operand transposed out of LDS (see fa_device.h).
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
+// Row sums D of fa_bwd_static, which takes no workspace: kStaticScratchRows
+// fp32 values (16 MiB) of device memory that every GPU the library runs on
+// holds from its first fa_bwd_static call until the process ends.
+static __device__ __align__(256) float scratch[fa::kStaticScratchRows];
+
 namespace fa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};  // scratch's address on each device, once looked up
+}  // namespace
+
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// array's address on a device comes from hipGetSymbolAddress with that device
+// current, looked up once per device and kept.
+hipError_t static_scratch(hipStream_t stream, float** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);  // the device the launches will run on
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 struct BwdArgs {
   const void* q;

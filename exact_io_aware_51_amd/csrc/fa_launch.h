@@ -68,6 +68,12 @@ hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s);   // E4M3 q, k, v; b
 // split keys (p.splits > 1, 16-bit): partials into p.part, then the merge into o / lse
 hipError_t launch_decode(const FwdProblem& p, hipStream_t s);       // Nq == 1
 hipError_t launch_split_merge(const FwdProblem& p, hipStream_t s);
+// Capacity of the static device scratch that holds fa_bwd_static's row sums
+// D (one fp32 per query row: B * H * N at most this).
+constexpr long long kStaticScratchRows = 1LL << 22;
+// That scratch's address on the device `stream` runs on (looked up once per
+// device; allocates nothing).
+hipError_t static_scratch(hipStream_t stream, float** out);
 // stage: 0 = row sums D, 1 = dK/dV, 2 = dQ
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only

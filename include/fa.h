@@ -27,7 +27,9 @@
  *  - Every pointer must be 16-byte aligned.  Outputs must not alias inputs.
  *  - The caller owns every buffer and keeps it alive until the work queued on
  *    `stream` has finished.  The library allocates, frees and caches no device
- *    memory and holds no mutable global state; calls are reentrant.
+ *    memory and holds no mutable global state; calls are reentrant.  (The one
+ *    exception is fa_bwd_static, which keeps its row sums in a fixed device
+ *    array instead of a caller's workspace.)
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is queued asynchronously; the library never synchronises.
  *  - Return value: FA_OK or a negative fa_status.  Arguments are validated
@@ -51,7 +53,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* NULL/misaligned pointer, bad size, non-finite scale, causal not 0/1 */
   FA_ERR_UNSUPPORTED = -2, /* a head dimension or dtype this library has no kernel for */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_bwd_workspace_bytes() */
-  FA_ERR_HIP = -4          /* the HIP runtime refused a launch (no device, bad stream, ...) */
+  FA_ERR_HIP = -4,         /* the HIP runtime refused a launch (no device, bad stream, ...) */
+  FA_ERR_TOO_LARGE = -5    /* fa_bwd_static only: B * H * N above FA_STATIC_SCRATCH_ROWS */
 } fa_status;
 
 /*
@@ -118,6 +121,28 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, c
 int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, const float *lse,
               const void *workspace, size_t workspace_bytes, void *dq,
               int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
+
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments, results and validation without the workspace, whose row sums D
+ * live in a fixed device array of FA_STATIC_SCRATCH_ROWS fp32 values (16 MiB)
+ * instead.  Every GPU the library runs on holds its own copy of that array
+ * from its first fa_bwd_static call until the process ends; the call itself
+ * allocates nothing.  Its address on a device is looked up once, on the
+ * first call whose `stream` runs on that device.
+ *   B * H * N above FA_STATIC_SCRATCH_ROWS returns FA_ERR_TOO_LARGE.
+ * All fa_bwd_static calls on one device share the array: calls that overlap
+ * in time on one GPU (concurrent streams) race and give wrong gradients;
+ * order them on one stream, or use fa_bwd with a workspace each.  Nothing
+ * needs clearing between calls: each call writes every row sum it reads.
+ */
+#define FA_STATIC_SCRATCH_ROWS (1 << 22)
+int fa_bwd_static(const void *q, const void *k, const void *v, const void *o,
+                  const void *dout, const float *lse,
+                  void *dq, void *dk, void *dv,
+                  int B, int H, int N, int d, float scale, int causal,
+                  fa_dtype dtype, void *stream);
 
 /*
  * Unequal query and key counts, and padded batches.  The pages tie the causal

@@ -42,7 +42,7 @@ def test_header_declares_the_abi():
                                   "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
                                   "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_fp8", "fa_fwd_kv_split",
                                   "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "fa_status_string",
-                                  "fa_version"])
+                                  "fa_version", "fa_bwd_static"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_status_strings(fa):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         s = fa.fa_status_string(st)
         assert s and s != "unknown status"
     assert fa.fa_status_string(12345) == "unknown status"
@@ -128,6 +128,36 @@ def test_fwd_rejects(fa, name, kw, want):
 @pytest.mark.parametrize("name,kw,want", BWD_BAD, ids=[x[0] for x in BWD_BAD])
 def test_bwd_rejects(fa, name, kw, want):
     assert _bwd(fa, **kw) == want
+
+
+def _bwd_static(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), dout=_ptr(4), lse=_ptr(5), dq=_ptr(6),
+             dk=_ptr(7), dv=_ptr(8), B=1, H=2, N=256, d=64, scale=0.125, causal=1, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_static(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                            a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+STATIC_BAD = [
+    ("null dout", dict(dout=None), -1), ("null lse", dict(lse=None), -1), ("misaligned dk", dict(dk=_ptr(7, 2)), -1),
+    ("d=32", dict(d=32), -2), ("N=0", dict(N=0), -1), ("causal 2", dict(causal=2), -1),
+    ("dq aliases q", dict(dq=_ptr(0)), -1), ("inf scale", dict(scale=float("inf")), -1),
+    # one row past the static scratch, and far past it; the addresses are never touched
+    ("B*H*N = capacity + 1", dict(B=1, H=1, N=(1 << 22) + 1), -5),
+    ("B*H*N = 6 x 700000", dict(B=2, H=3, N=700000), -5),
+]
+
+
+@pytest.mark.parametrize("name,kw,want", STATIC_BAD, ids=[x[0] for x in STATIC_BAD])
+def test_bwd_static_rejects(fa, name, kw, want):
+    assert _bwd_static(fa, **kw) == want
+
+
+def test_bwd_static_capacity_is_declared(fa):
+    text = open(HEADER).read()
+    assert re.search(r"#define FA_STATIC_SCRATCH_ROWS \(1 << 22\)", text)
+    assert fa.STATIC_SCRATCH_ROWS == 1 << 22
+    assert "fa_bwd_static" in fa.fa_status_string(fa.FA_ERR_TOO_LARGE)
 
 
 STAGE_BAD = [
@@ -351,6 +381,8 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd(fa) == fa.FA_ERR_HIP
     assert _fwd(fa, lse=None, causal=1, dtype=fa.FA_F32, scale=-1.0) == fa.FA_ERR_HIP
     assert _bwd(fa) == fa.FA_ERR_HIP
+    assert _bwd_static(fa) == fa.FA_ERR_HIP
+    assert _bwd_static(fa, B=1, H=1, N=1 << 22) == fa.FA_ERR_HIP  # exactly the capacity is accepted
     assert fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(9), 1 << 20, 1, 2, 256, 64, fa.FA_BF16, None) == fa.FA_ERR_HIP
     assert _fwd_kv(fa) == fa.FA_ERR_HIP
     assert _fwd_kv(fa, sq=None, sk=None, Nq=1) == fa.FA_ERR_HIP
