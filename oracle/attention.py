@@ -460,7 +460,8 @@ def attention_backward_dropout(q, k, v, do, scale, causal, p, seed, offset):
 #     (OFP8)", revision 1.0, 2023): one sign bit, four exponent bits with bias
 #     7, three mantissa bits; exponent field 0 encodes the subnormals
 #     m / 8 * 2^-6; the codes with all exponent and mantissa bits set are NaN;
-#     there are no infinities;
+#     there are no infinities.  Or all three hold E5M2 codes of the same
+#     specification (decoded by e5m2_decode below);
 #   * each tensor carries one real dequantisation factor, so the attention
 #     inputs are descale_q * E(q), descale_k * E(k), descale_v * E(v);
 #   * the result is the plain definition on those values: exact attention
@@ -477,11 +478,32 @@ def e4m3_decode(codes):
     return np.where((c & 127) == 127, np.nan, sign * mag)
 
 
-def attention_forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, scale, causal):
-    """O, LSE of exact attention on dequantised E4M3 inputs ([B, H, N, d] code arrays)."""
-    q = e4m3_decode(_codes(q8)) * float(descale_q)
-    k = e4m3_decode(_codes(k8)) * float(descale_k)
-    v = e4m3_decode(_codes(v8)) * float(descale_v)
+def e5m2_decode(codes):
+    """float64 values of uint8 OCP E5M2 codes (any array shape).
+
+    E5M2 (same specification): one sign bit, five exponent bits with bias 15,
+    two mantissa bits; exponent field 0 encodes the subnormals m / 4 * 2^-14;
+    exponent field 31 encodes infinity (mantissa 0) and NaN (mantissa != 0),
+    as in IEEE 754 binary formats."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >= 128, -1.0, 1.0)
+    e = (c >> 2) & 31
+    m = (c & 3).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 4.0, -14), np.ldexp(1.0 + m / 4.0, e - 15))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
+FP8_DECODERS = {"e4m3": e4m3_decode, "e5m2": e5m2_decode}
+
+
+def attention_forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, scale, causal, fmt="e4m3"):
+    """O, LSE of exact attention on dequantised 8-bit inputs ([B, H, N, d] code
+    arrays, all three in format `fmt`: "e4m3" or "e5m2")."""
+    dec = FP8_DECODERS[fmt]
+    q = dec(_codes(q8)) * float(descale_q)
+    k = dec(_codes(k8)) * float(descale_k)
+    v = dec(_codes(v8)) * float(descale_v)
     return attention_forward(q, k, v, scale, causal)
 
 

@@ -815,6 +815,85 @@ def pin_fp8_descale_invariances(orc):
     _close(o, np.full(o.shape, 0.5), 1e-14, "constant V = descale_v * 1")
 
 
+# E5M2 codes (same specification) as a second input format: IEEE-like, with
+# infinities at exponent field 31.
+def _e5m2_fixture():
+    def val(v):
+        return math.nan if v is None else float(v)  # "inf" / "-inf" strings parse as floats
+    with open(os.path.join(GOLDEN, "e5m2_values.json")) as f:
+        return {int(c, 16): val(v) for c, v in json.load(f)["values"].items()}
+
+
+def pin_e5m2_table(orc):
+    for code, want in _e5m2_fixture().items():
+        got = float(orc.e5m2_decode(np.array([code], dtype=np.uint8))[0])
+        if math.isnan(want):
+            assert math.isnan(got), f"e5m2 code {code:#04x} should be NaN, got {got}"
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), \
+                f"e5m2 code {code:#04x}: {got} != {want}"
+
+
+def pin_e5m2_library(orc):
+    """All 256 codes against torch's float8_e5m2 (the same OCP format)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    got = orc.e5m2_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "e5m2 NaN codes differ from torch"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "e5m2 values differ from torch"
+
+
+def pin_e5m2_order(orc):
+    """Codes 0x00..0x7c increase strictly up to +inf; 0x7d..0x7f are NaN; the
+    sign bit negates; each binade holds four codes that double across it."""
+    pos = orc.e5m2_decode(np.arange(125, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0) and pos[-1] == np.inf, "codes 0x00..0x7c must increase to +inf"
+    assert np.all(np.isnan(orc.e5m2_decode(np.arange(125, 128, dtype=np.uint8)))), "0x7d..0x7f are NaN"
+    neg = orc.e5m2_decode(np.arange(128, 253, dtype=np.uint8))
+    assert np.array_equal(neg, -pos), "the sign bit must negate"
+    normal = pos[4:124]
+    assert np.array_equal(normal[4:], 2.0 * normal[:-4]), "a step of four codes doubles a normal value"
+    sub = pos[:4]
+    assert np.array_equal(sub, np.arange(4) * sub[1]) and sub[1] == pos[4] / 4, "subnormals are even steps of 2^-16"
+
+
+def pin_fp8_e5m2_bruteforce(orc):
+    """Scalar loops over E5M2 fixture codes with three dequantisation factors."""
+    table = {c: v for c, v in _e5m2_fixture().items() if math.isfinite(v) and abs(v) <= 3.0}
+    codes = np.array(sorted(table), dtype=np.uint8)
+    r = _rng(73)
+    for causal, (N, d) in ((False, (5, 3)), (True, (6, 4))):
+        q8, k8, v8 = (codes[r.integers(0, len(codes), (1, 2, N, d))] for _ in range(3))
+        dq, dk, dv, scale = 0.5, 1.5, 0.25, 0.7
+        o, lse = orc.attention_forward_fp8(q8, k8, v8, dq, dk, dv, scale, causal, fmt="e5m2")
+        for h in range(2):
+            q = [[dq * table[int(x)] for x in row] for row in q8[0, h]]
+            k = [[dk * table[int(x)] for x in row] for row in k8[0, h]]
+            v = [[dv * table[int(x)] for x in row] for row in v8[0, h]]
+            bo, bl = _brute_head(q, k, v, scale, causal)
+            _close(o[0, h], bo, 1e-12, f"fp8 e5m2 brute O causal={causal}")
+            _close(lse[0, h], bl, 1e-12, f"fp8 e5m2 brute LSE causal={causal}")
+
+
+def pin_fp8_formats_agree(orc):
+    """Values that both formats hold exactly (powers of two in 2^-6..2^8 and
+    their 1.5 multiples) give the same attention through either decoder."""
+    r = _rng(74)
+    vals = np.array([s * m * 2.0 ** e for s in (1, -1) for m in (1.0, 1.5) for e in range(-6, 6)])
+    x = vals[r.integers(0, len(vals), (3, 1, 2, 11, 8))]
+    enc4 = {float(v): c for c, v in enumerate(orc.e4m3_decode(np.arange(256, dtype=np.uint8))) if np.isfinite(v)}
+    enc5 = {float(v): c for c, v in enumerate(orc.e5m2_decode(np.arange(256, dtype=np.uint8))) if np.isfinite(v)}
+    c4 = np.vectorize(lambda t: enc4[float(t)])(x).astype(np.uint8)
+    c5 = np.vectorize(lambda t: enc5[float(t)])(x).astype(np.uint8)
+    for causal in (False, True):
+        o4, l4 = orc.attention_forward_fp8(c4[0], c4[1], c4[2], 0.3, 0.2, 2.0, 0.5, causal, fmt="e4m3")
+        o5, l5 = orc.attention_forward_fp8(c5[0], c5[1], c5[2], 0.3, 0.2, 2.0, 0.5, causal, fmt="e5m2")
+        _close(o5, o4, 1e-14, f"formats agree O causal={causal}")
+        _close(l5, l4, 1e-14, f"formats agree LSE causal={causal}")
+
+
 ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pin_constant_v,
             pin_q_zero, pin_causal_row0_and_n1, pin_shift_invariance, pin_permutation,
             pin_online_recurrence, pin_scipy_logsumexp, pin_torch_autograd,
@@ -825,4 +904,5 @@ ALL_PINS = [pin_bruteforce_forward, pin_worked_example, pin_probability_rows, pi
             pin_sparse_torch_autograd, pin_sparse_finite_differences, pin_sparse_rows_match_full,
             pin_philox_known_answers, pin_dropout_p0_is_dense, pin_dropout_bruteforce, pin_dropout_keep_rate,
             pin_dropout_unbiased, pin_dropout_torch_autograd, pin_dropout_finite_differences,
-            pin_e4m3_table, pin_e4m3_library, pin_e4m3_order, pin_fp8_bruteforce, pin_fp8_descale_invariances]
+            pin_e4m3_table, pin_e4m3_library, pin_e4m3_order, pin_fp8_bruteforce, pin_fp8_descale_invariances,
+            pin_e5m2_table, pin_e5m2_library, pin_e5m2_order, pin_fp8_e5m2_bruteforce, pin_fp8_formats_agree]

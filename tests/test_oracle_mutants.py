@@ -61,8 +61,14 @@ MUTANTS = {
     "e4m3 subnormals as normals": ("np.where(e == 0, np.ldexp(m / 8.0, -6)", "np.where(e == -1, np.ldexp(m / 8.0, -6)"),
     "e4m3 subnormal exponent": ("np.ldexp(m / 8.0, -6)", "np.ldexp(m / 8.0, -7)"),
     "e4m3 NaN code": ("(c & 127) == 127", "(c & 127) == 126"),
-    "fp8 descale_v dropped": ("v = e4m3_decode(_codes(v8)) * float(descale_v)", "v = e4m3_decode(_codes(v8))"),
-    "fp8 k takes descale_q": ("k = e4m3_decode(_codes(k8)) * float(descale_k)", "k = e4m3_decode(_codes(k8)) * float(descale_q)"),
+    "fp8 descale_v dropped": ("v = dec(_codes(v8)) * float(descale_v)", "v = dec(_codes(v8))"),
+    "fp8 k takes descale_q": ("k = dec(_codes(k8)) * float(descale_k)", "k = dec(_codes(k8)) * float(descale_q)"),
+    "e5m2 exponent bias 16": ("np.ldexp(1.0 + m / 4.0, e - 15)", "np.ldexp(1.0 + m / 4.0, e - 16)"),
+    "e5m2 three mantissa bits": ("e = (c >> 2) & 31\n    m = (c & 3)", "e = (c >> 3) & 15\n    m = (c & 7)"),
+    "e5m2 subnormal exponent": ("np.ldexp(m / 4.0, -14)", "np.ldexp(m / 4.0, -15)"),
+    "e5m2 no infinities": ("np.where(m == 0, np.inf, np.nan)", "np.where(m == 0, np.nan, np.nan)"),
+    "e5m2 sign ignored": ("sign = np.where(c >= 128, -1.0, 1.0)\n    e = (c >> 2)", "sign = 1.0\n    e = (c >> 2)"),
+    "fp8 format ignored": ("dec = FP8_DECODERS[fmt]", "dec = e4m3_decode"),
     "kv dropped D term": ("ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))\n            dq[b, h, :a]",
                           "ds = p * dp\n            dq[b, h, :a]"),
 }
