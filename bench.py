@@ -529,8 +529,9 @@ def clock_under_load(name, dev, seconds=3.0):
             "source": "amd-smi metric --clock (mean over XCDs)"}
 
 
-def time_fwd_fp8(name, dev, iters=20, warmup=3):
-    """The forward of workload `name`'s shape on E4M3 inputs (fa_fwd_fp8), against the 8-bit matrix peak."""
+def time_fwd_fp8(name, dev, iters=20, warmup=3, fmt="e4m3"):
+    """The forward of workload `name`'s shape on 8-bit inputs of format `fmt` (fa_fwd_fp8_fmt), against the
+    8-bit matrix peak."""
     import math
 
     import torch
@@ -538,17 +539,18 @@ def time_fwd_fp8(name, dev, iters=20, warmup=3):
     import exact_io_aware_51_amd as fa
     from exact_io_aware_51_amd import workloads as W
     w = W.WORKLOADS[name]
-    q8, k8, v8, ds = W.fp8_inputs(w.B, w.H, w.N, w.d, w.seed, q_scale=w.q_scale, v_uniform=w.v_uniform)
+    q8, k8, v8, ds = W.fp8_inputs(w.B, w.H, w.N, w.d, w.seed, q_scale=w.q_scale, v_uniform=w.v_uniform, fmt=fmt)
+    code = {"e4m3": fa.FA_FP8_E4M3, "e5m2": fa.FA_FP8_E5M2}[fmt]
     q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
     def run():
-        st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H,
-                           w.N, w.d, w.scale, int(w.causal), ds[0], ds[1], ds[2], stream)
+        st = fa.fa_fwd_fp8_fmt(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+                               w.H, w.N, w.d, w.scale, int(w.causal), ds[0], ds[1], ds[2], code, stream)
         if st != 0:
-            raise RuntimeError(f"fa_fwd_fp8: {fa.fa_status_string(st)}")
+            raise RuntimeError(f"fa_fwd_fp8_fmt: {fa.fa_status_string(st)}")
     for _ in range(warmup):
         run()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
@@ -562,7 +564,7 @@ def time_fwd_fp8(name, dev, iters=20, warmup=3):
     tf = w.fwd_flops() / (ms * 1e-3) / 1e12
     assert math.isfinite(float(o.float().abs().max()))
     return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["e4m3"], 4),
-            "shape": f"e4m3 in, bf16 out, B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
+            "shape": f"{fmt} in, bf16 out, B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
 def main():
@@ -701,8 +703,9 @@ def main():
         out["fwd_workloads"] = fw
         f8 = {}
         for name in ("c3", "c4"):
-            log(f"bench: forward-only {name} shape on E4M3 inputs")
-            f8[name] = time_fwd_fp8(name, dev)
+            for fmt in ("e4m3", "e5m2"):
+                log(f"bench: forward-only {name} shape on {fmt.upper()} inputs")
+                f8[name if fmt == "e4m3" else f"{name}_e5m2"] = time_fwd_fp8(name, dev, fmt=fmt)
         out["fwd_fp8_workloads"] = f8
         log("bench: shader clock under the c4 forward")
         clk = clock_under_load("c4", dev)

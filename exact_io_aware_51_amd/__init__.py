@@ -2,7 +2,7 @@
 
 The functions named like the C entry points (fa_fwd, fa_bwd, fa_fwd_kv,
 fa_bwd_kv, fa_fwd_sparse, fa_bwd_sparse, fa_fwd_dropout, fa_bwd_dropout,
-fa_fwd_fp8, fa_fwd_kv_split, fa_bwd_workspace_bytes, ...) take raw device
+fa_fwd_fp8, fa_fwd_fp8_fmt, fa_fwd_kv_split, fa_bwd_workspace_bytes, ...) take raw device
 addresses and sizes exactly as include/fa.h declares them.  forward(), backward(), forward_kv(),
 backward_kv(), forward_sparse(), backward_sparse(), forward_dropout(),
 backward_dropout() and forward_fp8() are conveniences for torch tensors:
@@ -21,22 +21,24 @@ __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd
            "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
            "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
            "backward_kv", "forward_sparse", "backward_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "forward_dropout", "backward_dropout", "fa_fwd_fp8", "forward_fp8", "fa_fwd_kv_split",
+           "forward_dropout", "backward_dropout", "fa_fwd_fp8", "fa_fwd_fp8_fmt", "forward_fp8", "fa_fwd_kv_split",
            "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "fa_bwd_static", "STATIC_SCRATCH_ROWS",
+           "FA_FP8_E4M3", "FA_FP8_E5M2",
            "SPARSE_BLOCK", "library_path", "load"]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 SPARSE_BLOCK = 128  # rows and keys per block of a block-sparse mask (FA_SPARSE_BLOCK)
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5
 STATIC_SCRATCH_ROWS = 1 << 22  # capacity of fa_bwd_static's device array (FA_STATIC_SCRATCH_ROWS)
+FA_FP8_E4M3, FA_FP8_E5M2 = 0, 1  # fa_fp8_format
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_fwd_fp8", "fa_fwd_kv_split", "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint",
-           "fa_bwd_static", "fa_status_string", "fa_version")
+           "fa_fwd_fp8", "fa_fwd_fp8_fmt", "fa_fwd_kv_split", "fa_fwd_kv_split_workspace_bytes",
+           "fa_fwd_kv_split_hint", "fa_bwd_static", "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -87,6 +89,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dropout.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, f, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_fp8_fmt.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, f, f, f, i, vp]
+    lib.fa_fwd_fp8_fmt.restype = i
     lib.fa_fwd_kv_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i, i, vp, sz, i, vp]
     lib.fa_fwd_kv_split.restype = i
     lib.fa_fwd_kv_split_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -167,6 +171,11 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes
 
 def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, stream) -> int:
     return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, stream)
+
+
+def fa_fwd_fp8_fmt(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, fmt, stream) -> int:
+    return load().fa_fwd_fp8_fmt(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, fmt,
+                                 stream)
 
 
 def fa_fwd_kv_split(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, num_splits, workspace,
@@ -446,27 +455,33 @@ def backward_dropout(q, k, v, o, lse, dout, dropout_p, seed, offset=0, scale=Non
 
 
 def forward_fp8(q8, k8, v8, descale_q=1.0, descale_k=1.0, descale_v=1.0, scale=None, causal=False, need_lse=True,
-                stream=None):
-    """fa_fwd_fp8 on torch tensors: E4M3 codes (uint8 or float8_e4m3fn) [B, H, N, d] in, bf16 O and fp32 LSE out."""
+                stream=None, fmt="e4m3"):
+    """fa_fwd_fp8_fmt on torch tensors: 8-bit codes [B, H, N, d] in, bf16 O and fp32 LSE out.
+
+    fmt is "e4m3" (codes as uint8 or float8_e4m3fn) or "e5m2" (uint8 or float8_e5m2)."""
     import torch
+    formats = {"e4m3": (FA_FP8_E4M3, torch.float8_e4m3fn), "e5m2": (FA_FP8_E5M2, torch.float8_e5m2)}
+    if fmt not in formats:
+        raise ValueError(f"fmt must be one of {sorted(formats)}")
+    code, fp8_dtype = formats[fmt]
     codes = []
     for t in (q8, k8, v8):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError("tensors must live on a HIP device (no CPU path exists)")
-        if t.dtype == torch.float8_e4m3fn:
+        if t.dtype == fp8_dtype:
             t = t.view(torch.uint8)
         if t.dtype != torch.uint8 or t.dim() != 4 or not t.is_contiguous() or t.shape != q8.shape:
-            raise ValueError("q8, k8, v8 must be contiguous [B, H, N, d] E4M3 codes of one shape")
+            raise ValueError(f"q8, k8, v8 must be contiguous [B, H, N, d] {fmt.upper()} codes of one shape")
         codes.append(t)
     B, H, N, d = q8.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if need_lse else None
-    st = fa_fwd_fp8(codes[0].data_ptr(), codes[1].data_ptr(), codes[2].data_ptr(), o.data_ptr(),
-                    lse.data_ptr() if lse is not None else None, B, H, N, d, scale, int(bool(causal)),
-                    float(descale_q), float(descale_k), float(descale_v), _stream(q8, stream))
+    st = fa_fwd_fp8_fmt(codes[0].data_ptr(), codes[1].data_ptr(), codes[2].data_ptr(), o.data_ptr(),
+                        lse.data_ptr() if lse is not None else None, B, H, N, d, scale, int(bool(causal)),
+                        float(descale_q), float(descale_k), float(descale_v), code, _stream(q8, stream))
     if st != FA_OK:
-        raise FaError(st, "fa_fwd_fp8")
+        raise FaError(st, "fa_fwd_fp8_fmt")
     return o, lse
 
 

@@ -198,6 +198,15 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
 
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, float descale_q, float descale_k, float descale_v, void* stream) {
+  return fa_fwd_fp8_fmt(q, k, v, o, lse, B, H, N, d, scale, causal, descale_q, descale_k, descale_v, FA_FP8_E4M3,
+                        stream);
+}
+
+int fa_fwd_fp8_fmt(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int causal, float descale_q, float descale_k, float descale_v, fa_fp8_format fmt,
+                   void* stream) {
+  const int f = static_cast<int>(fmt);
+  if (f != FA_FP8_E4M3 && f != FA_FP8_E5M2) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if ((long long)B * H * N >= (1LL << 31)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -220,6 +229,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
   p.B = B; p.H = H; p.Nq = N; p.Nk = N; p.d = d;
   p.scale = (float)eff; p.causal = causal; p.descale_v = descale_v;
+  p.fp8_format = f == FA_FP8_E5M2 ? 1 : 0;
   (void)hipGetLastError();  // report only this launch's error
   return hip_status(fa::launch_fwd8(p, reinterpret_cast<hipStream_t>(stream)));
 }

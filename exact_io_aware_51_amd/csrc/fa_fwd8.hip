@@ -1,4 +1,4 @@
-// fa_fwd8.hip -- forward pass for OCP E4M3 (8-bit) inputs on the gfx950 matrix cores.
+// fa_fwd8.hip -- forward pass for OCP E4M3 or E5M2 (8-bit) inputs on the gfx950 matrix cores.
 //
 // The schedule is the 16-bit forward's (fa_fwd16.hip): a workgroup of four
 // waves owns 128 query rows of one (batch, head), 64-key K/V tiles stream
@@ -10,9 +10,10 @@
 // Matrix").  What differs is the operand format, the lower-precision path the
 // same page attributes to FlashAttention 3 ("FlashAttention 1 vs 2 vs 3"):
 //
-//  * Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands
-//    and unit block scales: 64 contraction elements per instruction at twice
-//    the 16-bit rate.  A lane supplies 32 bytes per operand, and the hardware
+//  * Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
+//    scales: 64 contraction elements per instruction at twice the 16-bit rate.
+//    The instruction takes each operand's format separately, so q, k and v
+//    may be E4M3 or E5M2 (FMT) while P, packed here, is always E4M3.  A lane supplies 32 bytes per operand, and the hardware
 //    pairs operand slots by (half-wave, byte), so the contraction index may be
 //    assigned to slots freely as long as both operands agree.
 //  * For P V the slot (h, e = 16 kb + 4 g + u) holds key 32 kb + 8 g + 4 h + u:
@@ -76,9 +77,14 @@ struct Tile8 {
   __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
 };
 
+// Operand format codes of the instruction: 0 = E4M3, 1 = E5M2.
+constexpr int kE4M3 = 0;
+constexpr int kE5M2 = 1;
+
+template <int FA, int FB>
 __device__ inline f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
-  // format 0 = E4M3 for both operands; block scales 127 = 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  // formats of A and B; block scales 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, 127, 0, 127);
 }
 
 // Four floats to four E4M3 bytes (round to nearest even), first in the low byte.
@@ -87,7 +93,7 @@ __device__ inline int pack_e4m3(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
   constexpr int BN = 64;  // keys per tile
   constexpr int KB = 2;   // 32-key blocks per tile
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
 
   auto pv = [&](int vstage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) oacc[mb] = mma8(vfrag(vstage, mb), pf, oacc[mb]);
+    for (int mb = 0; mb < MB; ++mb) oacc[mb] = mma8<FMT, kE4M3>(vfrag(vstage, mb), pf, oacc[mb]);
   };
   // registers 8 t .. 8 t + 7 of block kb (keys 32 kb + 8 g + 4 h + u, g = 2 t, 2 t + 1)
   // are P slots 16 kb + 8 t .. + 7, i.e. dwords 4 kb + 2 t and 4 kb + 2 t + 1
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sc[kb] = mma8(kfrag(KST, kb, ks), qf[ks], sc[kb]);
+        for (int kb = 0; kb < KB; ++kb) sc[kb] = mma8<FMT, FMT>(kfrag(KST, kb, ks), qf[ks], sc[kb]);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (FULL) {
         // unmasked tile: exponentiate against the running maximum first; a
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void fwd8_kernel(Fwd8Args a) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int FMT>
 static hipError_t launch_fwd8_t(const FwdProblem& p, hipStream_t stream) {
   Fwd8Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.o = p.o; a.lse = p.lse;
@@ -373,13 +379,18 @@ static hipError_t launch_fwd8_t(const FwdProblem& p, hipStream_t stream) {
   a.negate = sc < 0.0f;
   a.c = (sc < 0.0f ? -sc : sc) * kLog2e;
   a.descale_v = p.descale_v;
-  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(a.total), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL, FMT>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int FMT>
+static hipError_t launch_fwd8_f(const FwdProblem& p, hipStream_t s) {
+  if (p.d == 64) return p.causal ? launch_fwd8_t<64, true, FMT>(p, s) : launch_fwd8_t<64, false, FMT>(p, s);
+  return p.causal ? launch_fwd8_t<128, true, FMT>(p, s) : launch_fwd8_t<128, false, FMT>(p, s);
+}
+
 hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s) {
-  if (p.d == 64) return p.causal ? launch_fwd8_t<64, true>(p, s) : launch_fwd8_t<64, false>(p, s);
-  return p.causal ? launch_fwd8_t<128, true>(p, s) : launch_fwd8_t<128, false>(p, s);
+  return p.fp8_format == kE5M2 ? launch_fwd8_f<kE5M2>(p, s) : launch_fwd8_f<kE4M3>(p, s);
 }
 
 }  // namespace fa

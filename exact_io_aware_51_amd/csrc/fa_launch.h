@@ -29,8 +29,9 @@ struct FwdProblem {
   float drop_scale;
   float scale;
   int causal;
-  int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16 (launch_fwd8: E4M3 inputs, bf16 o)
+  int dtype;  // 0 = fp32, 1 = fp16, 2 = bf16 (launch_fwd8: 8-bit inputs, bf16 o)
   float descale_v;  // launch_fwd8 only: o = (P v) * descale_v; scale already holds descale_q * descale_k
+  int fp8_format;   // launch_fwd8 only: q, k, v codes are 0 = E4M3, 1 = E5M2
   // key splitting (16-bit only; splits <= 1: none): split s handles key tiles
   // [s * ceil(tiles / splits), ...) and writes fp32 partials into `part`
   // ([splits][B*H*Nq][d] outputs, then [splits][B*H*Nq] LSEs); a merge pass writes o / lse
@@ -64,7 +65,7 @@ struct BwdProblem {
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
 hipError_t launch_fwd16(const FwdProblem& p, hipStream_t s);  // bf16 / fp16 only
 hipError_t launch_fwd16_128(const FwdProblem& p, hipStream_t s);  // d = 128 (fa_fwd16_d128.hip)
-hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s);   // E4M3 q, k, v; bf16 o; Nq = Nk, dense
+hipError_t launch_fwd8(const FwdProblem& p, hipStream_t s);   // E4M3 or E5M2 q, k, v; bf16 o; Nq = Nk, dense
 // split keys (p.splits > 1, 16-bit): partials into p.part, then the merge into o / lse
 hipError_t launch_decode(const FwdProblem& p, hipStream_t s);       // Nq == 1
 hipError_t launch_split_merge(const FwdProblem& p, hipStream_t s);

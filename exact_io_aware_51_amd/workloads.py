@@ -116,14 +116,19 @@ def block_mask(B, H, N, keep, seed, block=128):
     return (torch.rand((B, H, nb, nb), generator=g) < keep).to(torch.uint8)
 
 
-def fp8_inputs(B, H, N, d, seed, q_scale=1.0, v_uniform=False):
-    """OCP E4M3 codes q8, k8, v8 (torch.uint8 [B,H,N,d]) and their dequantisation factors.
+FP8_FORMATS = {"e4m3": (torch.float8_e4m3fn, 448.0), "e5m2": (torch.float8_e5m2, 57344.0)}
+
+
+def fp8_inputs(B, H, N, d, seed, q_scale=1.0, v_uniform=False, fmt="e4m3"):
+    """OCP 8-bit codes q8, k8, v8 (torch.uint8 [B,H,N,d]) and their dequantisation factors.
 
     fp32 draws as in make_inputs (N(0,1) times q_scale; V optionally U(-1, 1)),
-    then per tensor: descale = the smallest power of two >= amax / 448, and the
-    code is the E4M3 rounding (to nearest even) of x / descale, so every code is
-    finite and the division is exact.  Returns (q8, k8, v8, (dq, dk, dv)).
+    then per tensor: descale = the smallest power of two >= amax / fmax (fmax =
+    448 for E4M3, 57344 for E5M2), and the code is the rounding (to nearest
+    even) of x / descale in format `fmt`, so every code is finite and the
+    division is exact.  Returns (q8, k8, v8, (dq, dk, dv)).
     """
+    fp8_dtype, fmax = FP8_FORMATS[fmt]
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
     shape = (B, H, N, d)
@@ -134,7 +139,24 @@ def fp8_inputs(B, H, N, d, seed, q_scale=1.0, v_uniform=False):
     codes, descales = [], []
     for x in (q * q_scale, k * q_scale, v * q_scale):
         amax = float(x.abs().max()) if x.numel() else 0.0
-        ds = 2.0 ** math.ceil(math.log2(amax / 448.0)) if amax > 0 else 1.0
-        codes.append((x / ds).to(torch.float8_e4m3fn).view(torch.uint8).contiguous())
+        ds = 2.0 ** math.ceil(math.log2(amax / fmax)) if amax > 0 else 1.0
+        codes.append((x / ds).to(fp8_dtype).view(torch.uint8).contiguous())
         descales.append(ds)
     return codes[0], codes[1], codes[2], tuple(descales)
+
+
+def fp8_wide_inputs(B, H, N, d, seed):
+    """E5M2 codes q8, k8, v8 (torch.uint8 [B,H,N,d]) whose magnitudes are
+    log-uniform over 2^-16 .. 2^15 with random signs (subnormals included,
+    no overflow), and dequantisation factors (2^-12, 2^-13, 2^-9) that keep
+    the scores at scale 0.125 within tens; code 0x01 (the smallest
+    subnormal) fills the first 7 x 3 corner of q's first head."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    codes = []
+    for _ in range(3):
+        mag = torch.exp2(torch.rand((B, H, N, d), generator=g) * 31.0 - 16.0)
+        sign = torch.where(torch.rand((B, H, N, d), generator=g) < 0.5, -1.0, 1.0)
+        codes.append((mag * sign).to(torch.float8_e5m2).view(torch.uint8).contiguous())
+    codes[0][0, 0, :7, :3] = 0x01
+    return codes[0], codes[1], codes[2], (2.0 ** -12, 2.0 ** -13, 2.0 ** -9)

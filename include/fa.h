@@ -309,6 +309,25 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                int B, int H, int N, int d, float scale, int causal,
                float descale_q, float descale_k, float descale_v, void *stream);
 
+/*
+ * The 8-bit forward with the input format chosen by the caller; fa_fwd_fp8 is
+ * this call with fmt = FA_FP8_E4M3.  With FA_FP8_E5M2, q, k and v hold OCP
+ * E5M2 codes (same specification: sign, 5 exponent bits with bias 15, 2
+ * mantissa bits, S.11111.00 = infinity, S.11111.mm with mm != 0 = NaN;
+ * largest finite magnitude 57344), the attention inputs are descale_x *
+ * E5M2(x), and everything else -- arguments, layout, output type, the E4M3
+ * rounding of the softmax weights and its error bound, errors -- is as for
+ * fa_fwd_fp8.  The codes must be finite: the outputs of a row whose scores or
+ * values meet an infinity or NaN are unspecified.  fmt outside the enum:
+ * FA_ERR_INVALID_ARG.
+ */
+typedef enum { FA_FP8_E4M3 = 0, FA_FP8_E5M2 = 1 } fa_fp8_format;
+
+int fa_fwd_fp8_fmt(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int N, int d, float scale, int causal,
+                   float descale_q, float descale_k, float descale_v,
+                   fa_fp8_format fmt, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -42,7 +42,7 @@ def test_header_declares_the_abi():
                                   "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
                                   "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_fp8", "fa_fwd_kv_split",
                                   "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "fa_status_string",
-                                  "fa_version", "fa_bwd_static"])
+                                  "fa_version", "fa_bwd_static", "fa_fwd_fp8_fmt"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -354,10 +354,13 @@ def test_fwd_kv_split_rejects(fa, name, kw, want):
 # 8-bit inputs: q, k, v are N*d bytes per head, o twice that (bf16).
 def _fwd8(fa, **kw):
     a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), lse=_ptr(4), B=1, H=2, N=256, d=128, scale=0.088,
-             causal=1, dq=0.01, dk=0.02, dv=0.5, stream=None)
+             causal=1, dq=0.01, dk=0.02, dv=0.5, stream=None, fmt=None)
     a.update(kw)
-    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"],
-                         a["causal"], a["dq"], a["dk"], a["dv"], a["stream"])
+    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"],
+            a["dq"], a["dk"], a["dv"])
+    if a["fmt"] is None:
+        return fa.fa_fwd_fp8(*args, a["stream"])
+    return fa.fa_fwd_fp8_fmt(*args, a["fmt"], a["stream"])
 
 
 FP8_BAD = [
@@ -371,9 +374,15 @@ FP8_BAD = [
 ]
 
 
+@pytest.mark.parametrize("fmt", [None, 0, 1], ids=["fp8", "fmt-e4m3", "fmt-e5m2"])
 @pytest.mark.parametrize("name,kw,want", FP8_BAD, ids=[x[0] for x in FP8_BAD])
-def test_fwd_fp8_rejects(fa, name, kw, want):
-    assert _fwd8(fa, **kw) == want
+def test_fwd_fp8_rejects(fa, name, kw, want, fmt):
+    assert _fwd8(fa, fmt=fmt, **kw) == want
+
+
+@pytest.mark.parametrize("fmt", [-1, 2, 255])
+def test_fwd_fp8_fmt_rejects_unknown_formats(fa, fmt):
+    assert _fwd8(fa, fmt=fmt) == -1
 
 
 @pytest.mark.skipif(not _no_gpu_here(), reason="would launch on fake addresses; only meaningful with no GPU")
@@ -397,6 +406,8 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _fwd_split(fa) == fa.FA_ERR_HIP
     assert _fwd_split(fa, ns=1, ws=None) == fa.FA_ERR_HIP
     assert _fwd8(fa, lse=None, causal=0, d=64, scale=-0.1) == fa.FA_ERR_HIP
+    assert _fwd8(fa, fmt=fa.FA_FP8_E5M2) == fa.FA_ERR_HIP
+    assert _fwd8(fa, fmt=fa.FA_FP8_E4M3, causal=0, d=64) == fa.FA_ERR_HIP
 
 
 def test_python_helpers_refuse_cpu_tensors(fa):

@@ -1,5 +1,5 @@
-"""The backward error model (gates.bwd_rounding_bound) against an emulation of
-the rounding scheme on the CPU.
+"""The backward error model (gates.bwd_rounding_bound) and the 8-bit forward's
+(gates.fp8_output_bound) against emulations of the rounding schemes on the CPU.
 
 The emulation takes the oracle's exact P, dP and dS and applies the roundings
 the 16-bit kernels perform (P before P V and O at the store in the forward; D
@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from exact_io_aware_51_amd import workloads as W
-from gates import bwd_rounding_bound, to_np
+from gates import ACC_ERR, bwd_rounding_bound, fp8_output_bound, to_np
 
 TYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -47,3 +47,47 @@ def test_emulated_rounding_within_bound(scale, dtype):
     # dropping D from dS is a real bug: the bound must not absorb it
     bad = _emulate(hq, hk, hv, hdo, terms, scale, dtype, drop_d=True)
     assert np.any(np.abs(bad[1] - ref[1][0, 0]) > bounds[1])
+
+
+def _emulate_fp8(q, k, v, scale, causal, stale, future=False):
+    """The 8-bit forward's roundings on one head: weights exp(s - m) taken
+    against a running maximum m = (true row maximum) - stale * ln 2 (the kernel
+    lets it lag by less than 8 binades), rounded to E4M3 (nearest even) before
+    the product with V, divided by the unrounded row sum, stored in bf16.
+    future=True plants a real bug: each row also sees the next key."""
+    n = q.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        lim = np.arange(n)[:, None] + (1 if future else 0)
+        s = np.where(np.arange(n)[None, :] <= lim, s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True) - stale * np.log(2.0)
+    p = torch.from_numpy(np.exp(s - m)).float()
+    rp = p.to(torch.float8_e4m3fn).double().numpy()
+    o = (rp @ v) / p.double().numpy().sum(axis=1, keepdims=True)
+    return torch.from_numpy(o).to(torch.bfloat16).double().numpy()
+
+
+def _fp8_cases():
+    wide = W.fp8_wide_inputs(1, 2, 640, 128, 31900)  # the GPU test's inputs
+    normal = W.fp8_inputs(1, 1, 320, 64, 63)
+    peaked = W.fp8_inputs(1, 1, 320, 64, 64, q_scale=4.0)
+    return {"e5m2-wide": (wide, "e5m2"), "e4m3": (normal, "e4m3"), "e4m3-peaked": (peaked, "e4m3")}
+
+
+@pytest.mark.parametrize("case", ["e5m2-wide", "e4m3", "e4m3-peaked"])
+@pytest.mark.parametrize("stale", [0.0, 7.5])
+def test_emulated_fp8_forward_within_bound(case, stale):
+    (q8, k8, v8, ds), fmt = _fp8_cases()[case]
+    dec = oracle.e5m2_decode if fmt == "e5m2" else oracle.e4m3_decode
+    q, k, v = (dec(x.numpy()) * f for x, f in zip((q8, k8, v8), ds))
+    scale = 0.125 if fmt == "e5m2" else 1.0 / 8.0
+    for causal in (False, True):
+        ro, _, bound, _ = fp8_output_bound(q, k, v, scale, causal, ACC_ERR[fmt])
+        for h in range(q.shape[1]):
+            got = _emulate_fp8(q[0, h], k[0, h], v[0, h], scale, causal, stale)
+            assert np.all(np.abs(got - ro[0, h]) <= bound[0, h]), f"{case} causal={causal} head {h}"
+            assert np.linalg.norm(got - ro[0, h]) <= 0.05 * np.linalg.norm(ro[0, h])
+    # a row that sees one key too many is a real bug: the bound must not absorb it
+    ro, _, bound, _ = fp8_output_bound(q, k, v, scale, True, ACC_ERR[fmt])
+    bad = _emulate_fp8(q[0, 0], k[0, 0], v[0, 0], scale, True, stale, future=True)
+    assert np.any(np.abs(bad - ro[0, 0]) > bound[0, 0])

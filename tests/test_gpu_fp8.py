@@ -1,27 +1,33 @@
-"""GPU parity for the 8-bit forward (fa_fwd_fp8).
+"""GPU parity for the 8-bit forward (fa_fwd_fp8, fa_fwd_fp8_fmt).
 
 The HIP path is compared with oracle.attention_forward_fp8, exact attention in
-float64 on the dequantised E4M3 inputs (reading: one dequantisation factor per
-tensor, bf16 output).  Two roundings separate the kernel from the definition,
-and the gates are derived from them:
+float64 on the dequantised E4M3 or E5M2 inputs (reading: one dequantisation
+factor per tensor, bf16 output).  Two roundings separate the kernel from the
+definition, and the gates are derived from them:
 
   * the 8-bit matrix product does not add its 64 products in fp32: measured on
-    gfx950 over 2^20 products of random full-range E4M3 codes, its error
-    reaches 2^-10.9 of the largest product magnitude.  Each score therefore
+    gfx950 over 2^20 products of random full-range codes, its error reaches
+    2^-10.75 (E4M3 x E4M3), 2^-11.44 (E5M2 x E5M2) and 2^-11.32 (E5M2 x E4M3)
+    of the largest product magnitude.  Each score therefore
     carries an error of at most delta_i = 2^-10 |scale| max_j sum_c |q_ic k_jc|
     (a 3x margin; d = 128 adds two such sums), which moves the LSE by at most
     delta_i and each weight p_ij by a relative 2 delta_i;
   * each softmax weight p is rounded to E4M3 before the product with V (round
     to nearest even: relative error <= 2^-4 for p >= 2^-6, absolute <= 2^-10
-    below).
+    below).  The kernel's weights are p_ij = P_ij l_i with its row sum l_i >=
+    1 / max_j P_ij (its running maximum never exceeds the true one), so an
+    absolute 2^-10 on p_ij is at most 2^-10 max_j P_ij on the normalised
+    weight.
 
 Hence |lse - r| <= delta_i + 2e-5 and, elementwise,
 
-    |o - r| <= (2^-4 + 2 delta_i) (P |V|)_ic + 2^-8 |r| + 2e-3 max|V_c|,
+    |o - r| <= (2^-4 + 2 delta_i + 2^-16) (P |V|)_ic + 2^-10 Pmax_i sum_j |v_jc|
+               + 2^-8 |r|,
 
 where (P |V|) is the oracle's attention over |V| (the weighted mean of |v| the
-rounding errors are bounded by), 2^-8 |r| covers the bf16 output rounding and
-the last term the weights below 2^-6 and fp32 noise.  A relative Frobenius
+relative roundings are bounded by), Pmax_i = max_j P_ij, the sum over j runs
+over all keys (a superset of the visible ones), 2^-8 |r| covers the bf16
+output rounding and 2^-16 the fp32 accumulation.  A relative Frobenius
 gate of 5% (the mean-square of a 3-bit-mantissa rounding is about 2.6%
 relative) keeps a wrong answer from hiding inside the elementwise bound.
 """
@@ -32,99 +38,84 @@ import torch
 import exact_io_aware_51_amd as fa
 import oracle
 from exact_io_aware_51_amd import workloads as W
-from gates import to_np
+from gates import ACC_ERR, fp8_output_bound, score_error_bound, to_np
 from gpu_util import announce, device
 
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 2, 300, 64), (2, 1, 512, 128), (1, 2, 1000, 128), (1, 1, 1000, 64), (1, 3, 129, 128), (1, 1, 1, 64)]
 SIDS = [f"B{b}H{h}N{n}d{d}" for b, h, n, d in SHAPES]
+FMTS = ["e4m3", "e5m2"]
+DECODE = {"e4m3": oracle.e4m3_decode, "e5m2": oracle.e5m2_decode}
 
 
-def _dequant(q8, k8, v8, ds):
-    return tuple(oracle.e4m3_decode(x.numpy()) * s for x, s in zip((q8, k8, v8), ds))
+def _dequant(q8, k8, v8, ds, fmt="e4m3"):
+    return tuple(DECODE[fmt](x.numpy()) * s for x, s in zip((q8, k8, v8), ds))
 
 
-def _check(o, lse, q8, k8, v8, ds, scale, causal, what, rows=None):
-    q, k, v = _dequant(q8, k8, v8, ds)
+def _check(o, lse, q8, k8, v8, ds, scale, causal, what, rows=None, fmt="e4m3"):
+    q, k, v = _dequant(q8, k8, v8, ds, fmt)
+    ro, rl, bound, delta = fp8_output_bound(q, k, v, scale, causal, ACC_ERR[fmt], rows)
     if rows is None:
-        ro, rl = oracle.attention_forward(q, k, v, scale, causal)
-        bound_pv, _ = oracle.attention_forward(q, k, np.abs(v), scale, causal)
         got, gl = to_np(o), to_np(lse)
     else:
         b, h, idx = rows
-        ro, rl = oracle.attention_forward_rows(q, k, v, scale, causal, b, h, idx)
-        bound_pv, _ = oracle.attention_forward_rows(q, k, np.abs(v), scale, causal, b, h, idx)
         got, gl = to_np(o)[b, h, idx], to_np(lse)[b, h, idx]
-        v = v[b, h][None, None]
-    vmax = np.max(np.abs(v), axis=-2, keepdims=True)  # per channel, over keys
-    if rows is not None:
-        vmax = vmax[0, 0]
-    delta = _score_error_bound(q, k, scale, rows)[..., None]
-    bound = (2.0 ** -4 + 2.0 * delta) * bound_pv + 2.0 ** -8 * np.abs(ro) + 2e-3 * vmax
     assert np.all(np.isfinite(got)), f"{what}: non-finite O"
     excess = np.abs(got - ro) - bound
     assert excess.max() <= 0, f"{what}: O outside the E4M3 rounding bound by {excess.max():.3e}"
     rel = np.linalg.norm(got - ro) / max(np.linalg.norm(ro), 1e-300)
     assert rel <= 0.05, f"{what}: relative Frobenius error {rel:.3e} > 5e-2"
-    lexcess = np.abs(gl - rl) - (delta[..., 0] + 2e-5)
+    lexcess = np.abs(gl - rl) - (delta + 2e-5)
     assert lexcess.max() <= 0, f"{what}: LSE outside its bound by {lexcess.max():.3e}"
     return rel
 
 
-def _score_error_bound(q, k, scale, rows=None):
-    """delta_i = 2^-10 |scale| max_j sum_c |q_ic| |k_jc| per row (over all keys: a valid, looser bound)."""
-    if rows is not None:
-        b, h, idx = rows
-        return 2.0 ** -10 * abs(scale) * np.max(np.abs(q[b, h, idx]) @ np.abs(k[b, h]).T, axis=1)
-    out = np.empty(q.shape[:3])
-    for b in range(q.shape[0]):
-        for h in range(q.shape[1]):
-            out[b, h] = 2.0 ** -10 * abs(scale) * np.max(np.abs(q[b, h]) @ np.abs(k[b, h]).T, axis=1)
-    return out
-
-
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", SHAPES, ids=SIDS)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_fwd_fp8_matches_oracle(causal, shape):
+def test_fwd_fp8_matches_oracle(causal, shape, fmt):
     dev = device()
     B, H, N, d = shape
-    seed = 31000 + N + d
-    announce("fwd_fp8", causal, shape, seed)
-    q8, k8, v8, ds = W.fp8_inputs(B, H, N, d, seed)
+    seed = 31000 + N + d + (0 if fmt == "e4m3" else 50)
+    announce("fwd_fp8", fmt, causal, shape, seed)
+    q8, k8, v8, ds = W.fp8_inputs(B, H, N, d, seed, fmt=fmt)
     scale = 1.0 / float(np.sqrt(d))
-    o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=scale, causal=causal)
+    o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=scale, causal=causal, fmt=fmt)
     torch.cuda.synchronize()
-    rel = _check(o, lse, q8, k8, v8, ds, scale, causal, f"fwd_fp8 causal={causal} {shape}")
-    print(f"fp8 {shape} causal={causal}: rel Frobenius {rel:.4f}")
+    rel = _check(o, lse, q8, k8, v8, ds, scale, causal, f"fwd_fp8 {fmt} causal={causal} {shape}", fmt=fmt)
+    print(f"fp8 {fmt} {shape} causal={causal}: rel Frobenius {rel:.4f}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("d", [64, 128])
-def test_fp8_scales_and_signs(d):
+def test_fp8_scales_and_signs(d, fmt):
     """Negative scale (the sign flip of q's codes), a non-trivial factor on each tensor, and peaked rows."""
     dev = device()
-    announce("fp8 scales", d)
-    q8, k8, v8, ds = W.fp8_inputs(1, 2, 700, d, 31500 + d, q_scale=4.0)
+    announce("fp8 scales", fmt, d)
+    q8, k8, v8, ds = W.fp8_inputs(1, 2, 700, d, 31500 + d, q_scale=4.0, fmt=fmt)
     ds = (ds[0] * 0.5, ds[1] * 3.0, ds[2] * 0.25)
     for scale in (-0.3 / np.sqrt(d), 0.7 / np.sqrt(d)):
         for causal in (False, True):
-            o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=scale, causal=causal)
+            o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=scale, causal=causal, fmt=fmt)
             torch.cuda.synchronize()
-            _check(o, lse, q8, k8, v8, ds, scale, causal, f"fp8 d={d} scale={scale:.3f} causal={causal}")
+            _check(o, lse, q8, k8, v8, ds, scale, causal, f"fp8 {fmt} d={d} scale={scale:.3f} causal={causal}",
+                   fmt=fmt)
 
 
-def test_fp8_matches_bf16_path_on_the_same_values():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp8_matches_bf16_path_on_the_same_values(fmt):
     """The dequantised inputs are exact in bf16, so both paths compute the same attention; only P's rounding differs."""
     dev = device()
-    announce("fp8 vs bf16")
-    q8, k8, v8, ds = W.fp8_inputs(2, 2, 1024, 128, 31600)
-    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in _dequant(q8, k8, v8, ds))
-    assert all(np.array_equal(t.double().numpy(), x) for t, x in zip((q, k, v), _dequant(q8, k8, v8, ds)))
-    o8, l8 = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, causal=True)
+    announce("fp8 vs bf16", fmt)
+    q8, k8, v8, ds = W.fp8_inputs(2, 2, 1024, 128, 31600, fmt=fmt)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in _dequant(q8, k8, v8, ds, fmt))
+    assert all(np.array_equal(t.double().numpy(), x) for t, x in zip((q, k, v), _dequant(q8, k8, v8, ds, fmt)))
+    o8, l8 = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, causal=True, fmt=fmt)
     o16, l16 = fa.forward(q.to(dev), k.to(dev), v.to(dev), causal=True)
     torch.cuda.synchronize()
-    q64, k64, _ = _dequant(q8, k8, v8, ds)
-    delta = _score_error_bound(q64, k64, 1.0 / np.sqrt(128.0))
+    q64, k64, _ = _dequant(q8, k8, v8, ds, fmt)
+    delta = score_error_bound(q64, k64, 1.0 / np.sqrt(128.0), ACC_ERR[fmt])
     assert np.all(np.abs(to_np(l8) - to_np(l16)) <= delta + 1e-3)
     rel = float((o8.float() - o16.float()).norm() / o16.float().norm())
     assert rel <= 0.05, f"fp8 vs bf16 relative difference {rel:.3e}"
@@ -139,17 +130,48 @@ def test_fp8_zero_value_factor():
     assert torch.all(o == 0) and torch.all(torch.isfinite(lse))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape,causal", [((2, 32, 8192, 64), False), ((1, 8, 32768, 128), True)],
                          ids=["c3-shape", "c4-shape"])
-def test_fp8_long_rows_sampled(shape, causal):
-    """The long-sequence shapes in E4M3, checked on sampled rows (first, last, ragged middle) of two heads."""
+def test_fp8_long_rows_sampled(shape, causal, fmt):
+    """The long-sequence shapes in 8 bits, checked on sampled rows (first, last, ragged middle) of two heads."""
     dev = device()
     B, H, N, d = shape
-    announce("fp8 long", shape, causal)
-    q8, k8, v8, ds = W.fp8_inputs(B, H, N, d, 31800 + N, q_scale=0.5 if d == 64 else 1.0, v_uniform=d == 128)
+    announce("fp8 long", fmt, shape, causal)
+    q8, k8, v8, ds = W.fp8_inputs(B, H, N, d, 31800 + N, q_scale=0.5 if d == 64 else 1.0, v_uniform=d == 128, fmt=fmt)
     scale = 1.0 / float(np.sqrt(d))
-    o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=scale, causal=causal)
+    o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=scale, causal=causal, fmt=fmt)
     torch.cuda.synchronize()
     rows = [0, 1, 127, 128, N // 2 + 37, N - 129, N - 1]
     for b, h in ((0, 0), (B - 1, H - 1)):
-        _check(o, lse, q8, k8, v8, ds, scale, causal, f"fp8 {shape} b={b} h={h}", rows=(b, h, rows))
+        _check(o, lse, q8, k8, v8, ds, scale, causal, f"fp8 {fmt} {shape} b={b} h={h}", rows=(b, h, rows), fmt=fmt)
+
+
+def test_fp8_e5m2_wide_range():
+    """E5M2's reason to exist: values spread over many binades (log-uniform magnitudes
+    2^-16 .. 2^15 with random signs, subnormals included) in q, k and v."""
+    dev = device()
+    announce("fp8 e5m2 wide range")
+    q8, k8, v8, ds = W.fp8_wide_inputs(1, 2, 640, 128, 31900)
+    for causal in (False, True):
+        o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=0.125, causal=causal, fmt="e5m2")
+        torch.cuda.synchronize()
+        _check(o, lse, q8, k8, v8, ds, 0.125, causal, f"fp8 e5m2 wide causal={causal}", fmt="e5m2")
+
+
+def test_fp8_fmt_argument_is_honoured():
+    """The same bytes read as E4M3 and as E5M2 are different numbers: each call matches its own format's oracle."""
+    dev = device()
+    announce("fp8 fmt honoured")
+    g = torch.Generator().manual_seed(31950)
+    # magnitudes 0x28..0x50: E4M3 0.25 .. 8, E5M2 2^-5 .. 32; random signs
+    q8, k8, v8 = ((torch.randint(0x28, 0x51, (1, 1, 256, 64), generator=g)
+                   | (torch.randint(0, 2, (1, 1, 256, 64), generator=g) << 7)).to(torch.uint8) for _ in range(3))
+    ds = (0.125, 0.125, 1.0)
+    outs = {}
+    for fmt in FMTS:
+        o, lse = fa.forward_fp8(q8.to(dev), k8.to(dev), v8.to(dev), *ds, scale=0.125, causal=False, fmt=fmt)
+        torch.cuda.synchronize()
+        _check(o, lse, q8, k8, v8, ds, 0.125, False, f"fp8 bytes as {fmt}", fmt=fmt)
+        outs[fmt] = o.float()
+    assert not torch.allclose(outs["e4m3"], outs["e5m2"], rtol=0.1, atol=0.1)
