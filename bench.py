@@ -89,65 +89,6 @@ STEP_KERNELS = {"fwd16_kernel": "fwd", "bwd_pre_kernel": "bwd_rowsum", "dkdv16_k
                 "dq16_kernel": "bwd_dq"}
 
 
-def _counter_per_dispatch(run_dir, counter):
-    """{kernel name: mean per-dispatch value of `counter`} from a rocprofv3 --pmc CSV run directory."""
-    import csv
-    import glob
-    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
-    per = {}  # (kernel, dispatch) -> summed value
-    for fn in files:
-        with open(fn, newline="") as f:
-            for row in csv.DictReader(f):
-                if row.get("Counter_Name") != counter:
-                    continue
-                key = (row["Kernel_Name"], row["Dispatch_Id"])
-                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
-    out = {}
-    for (kname, _), v in per.items():
-        out.setdefault(kname, []).append(v)
-    return {k: sum(v) / len(v) for k, v in out.items()}
-
-
-def write_traffic(prof_dir, w):
-    """Build profiles/traffic.json from four rocprofv3 --pmc runs under prof_dir:
-    pmc_traffic_FETCH_SIZE, pmc_traffic_WRITE_SIZE (the step, bench.py --no-fwd-workloads) and
-    pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE (bench.py --copy-calibration 1024)."""
-    copy_bytes = 1024 << 20
-    cf = _counter_per_dispatch(os.path.join(prof_dir, "pmc_copy_FETCH_SIZE"), "FETCH_SIZE")
-    cw = _counter_per_dispatch(os.path.join(prof_dir, "pmc_copy_WRITE_SIZE"), "WRITE_SIZE")
-    copy_name = next(k for k in cf if "copyBuffer" in k)
-    fetch_factor = copy_bytes / (cf[copy_name] * 1024.0)
-    write_factor = copy_bytes / (cw[copy_name] * 1024.0)
-    sf = _counter_per_dispatch(os.path.join(prof_dir, "pmc_traffic_FETCH_SIZE"), "FETCH_SIZE")
-    sw = _counter_per_dispatch(os.path.join(prof_dir, "pmc_traffic_WRITE_SIZE"), "WRITE_SIZE")
-    models = kernel_models(w)
-    kernels = {}
-    for kname, fkib in sf.items():
-        stage = next((v for k, v in STEP_KERNELS.items() if k in kname), None)
-        if stage is None:
-            continue
-        wkib = sw.get(kname, 0.0)
-        kernels[stage] = {"kernel_symbol": kname, "fetch_kib_per_dispatch": round(fkib, 1),
-                          "write_kib_per_dispatch": round(wkib, 1),
-                          "hbm_bytes_per_launch": int(round(fkib * 1024 * fetch_factor + wkib * 1024 * write_factor)),
-                          "algorithmic_bytes_per_launch": models[stage]["bytes"]}
-    t = {"source_digest": source_digest(),
-         "workload": f"{w.name}: {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}",
-         "calibration": {"copy_kernel": copy_name, "copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
-                         "copy_fetch_kib": round(cf[copy_name], 1), "copy_write_kib": round(cw[copy_name], 1),
-                         "fetch_factor": round(fetch_factor, 4), "write_factor": round(write_factor, 4)},
-         "kernels": kernels}
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(t, f, indent=1)
-        f.write("\n")
-    for stage, e in kernels.items():
-        log(f"{stage}: fetch {e['fetch_kib_per_dispatch']} KiB, write {e['write_kib_per_dispatch']} KiB, "
-            f"HBM {e['hbm_bytes_per_launch'] / 1e6:.1f} MB vs algorithmic {e['algorithmic_bytes_per_launch'] / 1e6:.1f} MB")
-    log(f"wrote {TRAFFIC_FILE} (factors {fetch_factor:.4f} / {write_factor:.4f})")
-
-
 # --------------------------------------------------------------- counter reports
 N_XCD, N_CU, MFMA_FLOP_PER_CU_CLK = 8, 256, 4096   # MI355X: 2.5 PFLOP/s dense bf16 = 256 CU x 2.4 GHz x 4096
 COUNTER_PASSES = [
@@ -293,7 +234,102 @@ def write_counter_report(prof_dir, w, cal_dir):
     with open(base + ".md", "w") as f:
         f.write(_counter_markdown(rep))
     log(f"wrote {base}.json / .md")
+    if w.mode == "fwd+bwd":
+        # the HBM bytes the bench line reports as roofline.traffic, tied to these sources
+        t = {"source_digest": rep["source_digest"], "workload": rep["workload"],
+             "from": f"profiles/{w.name}_counters.json (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated)",
+             "calibration": rep["calibration"],
+             "kernels": {st: {"kernel_symbol": r["kernel_symbol"],
+                              "fetch_kib_per_dispatch": r["raw_counters_per_dispatch"].get("FETCH_SIZE"),
+                              "write_kib_per_dispatch": r["raw_counters_per_dispatch"].get("WRITE_SIZE"),
+                              "hbm_bytes_per_launch": r["hbm_bytes"],
+                              "algorithmic_bytes_per_launch": r["algorithmic_bytes"]} for st, r in rows.items()}}
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+            f.write("\n")
+        log(f"wrote {TRAFFIC_FILE}")
     return rep
+
+
+STEP_LABELS = {"fwd": "fa_fwd", "bwd_rowsum": "fa_bwd_rowsum", "bwd_dkdv": "fa_bwd_dkdv", "bwd_dq": "fa_bwd_dq"}
+
+
+def write_trace_summary(trace_dir, w, warmup, steps, bench_log=None):
+    """profiles/<workload>_step_kernel_stats.md from a rocprofv3 --kernel-trace --stats run of
+    `bench.py --steps STEPS --warmup WARMUP --no-cpu-baseline`: the step is timed first, so the
+    first WARMUP + STEPS dispatches of each step kernel are the step's, the last STEPS of them timed."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
+    rows = list(csv.DictReader(open(files[0], newline="")))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    # per stage, the matching kernel dispatched first is the step's (other workloads' kernels come later)
+    step_kernel = {}
+    for r in rows:
+        stage = next((v for k, v in STEP_KERNELS.items() if k in r["Kernel_Name"]), None)
+        if stage is not None and stage not in step_kernel:
+            step_kernel[stage] = r["Kernel_Name"]
+    models = kernel_models(w)
+    n = warmup + steps
+    lines, total = [], 0.0
+    for stage, kname in step_kernel.items():
+        durs = by[kname]
+        if len(durs) < n:
+            raise SystemExit(f"{kname}: {len(durs)} dispatches, fewer than warmup + steps = {n}")
+        timed = durs[warmup:n]
+        avg = sum(timed) / steps
+        total += avg
+        lines.append((stage, kname, avg, min(timed), max(timed), models[stage]["flops"] / (avg * 1e-6) / 1e12))
+    lines.sort(key=lambda x: -x[2])
+    events = {}
+    if bench_log:  # the JSON line the profiled bench.py printed: its HIP-event figures for the same dispatches
+        with open(bench_log) as f:
+            line = next(x for x in f if x.startswith("{"))
+        events = {k: v["ms"] * 1e3 for k, v in json.loads(line)["kernels"].items()}
+    cmd = f"python3 bench.py --steps {steps} --warmup {warmup} --no-cpu-baseline"
+    L = [f"# Kernel trace of the bench step: workload {w.name}, {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} "
+         f"{'causal' if w.causal else 'non-causal'}", "",
+         "Commands (from the repository root on the MI355X box, `cd /tmp && export TMPDIR=/tmp` first; DIR is an "
+         "output folder):", "", "```",
+         f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR -o run -- {cmd} > LOG",
+         f"python3 bench.py --trace-summary-from DIR --bench-log LOG --steps {steps} --warmup {warmup}"
+         "   # writes this file",
+         "```", "",
+         f"bench.py times the step first ({warmup} warm-up + {steps} timed steps), so the first {n} dispatches of "
+         f"each step kernel are the step's; the table averages the {steps} timed ones. Algorithmic TFLOP/s "
+         "(causal-adjusted flops per launch over the traced duration) is what bench.py's roofline reports for the "
+         "slowest kernel from HIP events; the last column is bench.py's own HIP-event timing of the same dispatches "
+         "in this profiled run. The profiler slows the kernels: an unprofiled run of the same command is faster.",
+         "",
+         f"Source digest of the kernels traced: `{source_digest()}`.", "",
+         "| stage | kernel | avg us | min us | max us | share of step | algorithmic TFLOP/s | of 2.5 PF "
+         "| HIP events, same run (us) |",
+         "|---|---|---|---|---|---|---|---|---|"]
+    for stage, kname, avg, mn, mx, tf in lines:
+        ev = f"{events[stage]:.1f}" if stage in events else ""
+        L.append(f"| {STEP_LABELS[stage]} | `{kname}` | {avg:.1f} | {mn:.1f} | {mx:.1f} | {100 * avg / total:.1f}% | "
+                 f"{tf:.1f} | {tf / PEAK_TFLOPS[w.dtype]:.4f} | {ev} |")
+    L += ["", f"Step (sum of the kernels' averages): {total:.1f} us; "
+              f"{sum(m['flops'] for m in models.values()) / (total * 1e-6) / 1e12:.1f} TFLOP/s over kernel time.", ""]
+    sfiles = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if sfiles:
+        L += ["All dispatches of this library's kernels in the run (rocprofv3 `--stats`), including the forward-only "
+              "lines of the other workloads that bench.py times after the step:", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        for r in csv.DictReader(open(sfiles[0], newline="")):
+            if "fa::" in r["Name"] or "_ZN2fa" in r["Name"]:
+                L.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        L.append("")
+    out = os.path.join(ROOT, "profiles", f"{w.name}_step_kernel_stats.md")
+    with open(out, "w") as f:
+        f.write("\n".join(L))
+    log(f"wrote {out}")
 
 
 def _counter_markdown(rep):
@@ -580,20 +616,26 @@ def main():
                     help="diagnostic: time only the forward kernel of this workload (c1..c5), one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="diagnostic: run a plain device copy of MIB MiB five times (counter calibration)")
-    ap.add_argument("--traffic-from", default=None, metavar="DIR",
-                    help="write profiles/traffic.json from the rocprofv3 --pmc runs under DIR (no GPU needed)")
+    ap.add_argument("--trace-summary-from", default=None, metavar="DIR",
+                    help="write profiles/<workload>_step_kernel_stats.md from a rocprofv3 --kernel-trace --stats run "
+                         "of bench.py --steps S --warmup W --no-cpu-baseline under DIR (pass the same S and W; "
+                         "no GPU needed)")
+    ap.add_argument("--bench-log", default=None, metavar="LOG",
+                    help="with --trace-summary-from: the profiled bench.py's output, for its HIP-event figures")
     ap.add_argument("--counters-from", default=None, metavar="DIR",
                     help="write profiles/<workload>_counters.{json,md} from the rocprofv3 runs under DIR "
-                         "(trace/, pmc1..pmc4; see WORKLOAD_CMDS) with --calibration-from CAL (no GPU needed)")
+                         "(trace/, pmc1..pmc4; see WORKLOAD_CMDS) with --calibration-from CAL (no GPU needed); "
+                         "for the step workload also profiles/traffic.json")
     ap.add_argument("--calibration-from", default=None, metavar="CAL")
     args = ap.parse_args()
     if args.counters_from:
         from exact_io_aware_51_amd import workloads as W
         write_counter_report(args.counters_from, W.WORKLOADS[args.workload], args.calibration_from)
         return
-    if args.traffic_from:
+    if args.trace_summary_from:
         from exact_io_aware_51_amd import workloads as W
-        write_traffic(args.traffic_from, W.WORKLOADS[args.workload])
+        write_trace_summary(args.trace_summary_from, W.WORKLOADS[args.workload], args.warmup, args.steps,
+                            args.bench_log)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
