@@ -254,7 +254,7 @@ def write_counter_report(prof_dir, w, cal_dir):
 STEP_LABELS = {"fwd": "fa_fwd", "bwd_rowsum": "fa_bwd_rowsum", "bwd_dkdv": "fa_bwd_dkdv", "bwd_dq": "fa_bwd_dq"}
 
 
-def write_trace_summary(trace_dir, w, warmup, steps, bench_log=None):
+def write_trace_summary(trace_dir, w, warmup, steps, bench_log=None, out_dir=None):
     """profiles/<workload>_step_kernel_stats.md from a rocprofv3 --kernel-trace --stats run of
     `bench.py --steps STEPS --warmup WARMUP --no-cpu-baseline`: the step is timed first, so the
     first WARMUP + STEPS dispatches of each step kernel are the step's, the last STEPS of them timed."""
@@ -326,7 +326,7 @@ def write_trace_summary(trace_dir, w, warmup, steps, bench_log=None):
                 L.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                          f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
         L.append("")
-    out = os.path.join(ROOT, "profiles", f"{w.name}_step_kernel_stats.md")
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{w.name}_step_kernel_stats.md")
     with open(out, "w") as f:
         f.write("\n".join(L))
     log(f"wrote {out}")
@@ -484,6 +484,14 @@ class Runner:
                                    *self.dims, w.scale, int(w.causal), self.code, self.stream), "fa_bwd_dq")
 
 
+def _spread(times_ms):
+    """Median and minimum of per-launch times (ms)."""
+    t = sorted(times_ms)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return {"ms_median": round(med, 4), "ms_min": round(t[0], 4)}
+
+
 def time_fwd_only(name, dev, iters=20, warmup=3):
     import torch
 
@@ -499,9 +507,11 @@ def time_fwd_only(name, dev, iters=20, warmup=3):
         r.fwd()
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
-    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)) / iters
+    times = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]
+    ms = sum(times) / iters
     tf = w.fwd_flops() / (ms * 1e-3) / 1e12
-    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
+    return {"ms": round(ms, 4), **_spread(times), "tflops": round(tf, 1),
+            "frac_of_peak": round(tf / PEAK_TFLOPS[w.dtype], 4),
             "shape": f"{w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
@@ -596,10 +606,12 @@ def time_fwd_fp8(name, dev, iters=20, warmup=3, fmt="e4m3"):
         run()
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
-    ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)) / iters
+    times = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]
+    ms = sum(times) / iters
     tf = w.fwd_flops() / (ms * 1e-3) / 1e12
     assert math.isfinite(float(o.float().abs().max()))
-    return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["e4m3"], 4),
+    return {"ms": round(ms, 4), **_spread(times), "tflops": round(tf, 1),
+            "frac_of_peak": round(tf / PEAK_TFLOPS["e4m3"], 4),
             "shape": f"{fmt} in, bf16 out, B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
@@ -692,9 +704,10 @@ def main():
     step_flops = sum(m["flops"] for m in models.values())
     kernels = {}
     for i, (name, _) in enumerate(stages):
-        ms = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
+        times = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]
+        ms = sum(times) / K
         m = models[name]
-        kernels[name] = {"ms": round(ms, 4), "tflops": round(m["flops"] / (ms * 1e-3) / 1e12, 1),
+        kernels[name] = {"ms": round(ms, 4), **_spread(times), "tflops": round(m["flops"] / (ms * 1e-3) / 1e12, 1),
                          "gbs": round(m["bytes"] / (ms * 1e-3) / 1e9, 1)}
     event_ms = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(K)) / K
     dom = max(kernels, key=lambda n: kernels[n]["ms"])

@@ -1,0 +1,83 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic cost model, the timing
+summary helpers, the refusal of more than one GPU, and the kernel-trace summary
+written from a rocprofv3 trace."""
+import csv
+import importlib.util
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_cost_model_of_the_step(bench):
+    """Per-launch figures for B=2 H=16 N=4096 d=128 causal bf16, written out by hand."""
+    from exact_io_aware_51_amd import workloads as W
+    m = bench.kernel_models(W.WORKLOADS["c5"])
+    heads, n, d = 32, 4096, 128
+    nn = n * n // 2 * d * heads                     # causal half of N^2 d per head
+    t = n * d * 2 * heads                           # one bf16 tensor
+    r = 4 * n * heads                               # one fp32 row vector
+    assert m["fwd"] == {"flops": 4 * nn, "bytes": 4 * t + r}
+    assert m["bwd_dkdv"] == {"flops": 8 * nn, "bytes": 6 * t + 2 * r}
+    assert m["bwd_dq"] == {"flops": 2 * nn, "bytes": 5 * t + 2 * r}
+    assert m["bwd_rowsum"]["bytes"] == 2 * t + r
+    assert sum(k["flops"] for k in m.values()) == pytest.approx(14 * nn + 2.0 * n * d * heads)
+    assert m["bwd_dkdv"]["flops"] == 274877906944 and m["bwd_dkdv"]["bytes"] == 202375168
+
+
+def test_spread(bench):
+    assert bench._spread([3.0, 1.0, 2.0]) == {"ms_median": 2.0, "ms_min": 1.0}
+    assert bench._spread([4.0, 1.0, 3.0, 2.0]) == {"ms_median": 2.5, "ms_min": 1.0}
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def _write_trace(path, dispatches):
+    os.makedirs(path)
+    with open(os.path.join(path, "run_kernel_trace.csv"), "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 0
+        for i, (name, us) in enumerate(dispatches):
+            wr.writerow([i + 1, name, t, t + int(us * 1000)])
+            t += int(us * 1000) + 5000
+
+
+def test_trace_summary_takes_the_step_kernels(bench, tmp_path):
+    """The step's kernels are the first of their kind; a later forward of another
+    workload (same stage name, other instantiation) must not be taken for the step's."""
+    from exact_io_aware_51_amd import workloads as W
+    fwd, pre = "_ZN2fa12fwd16_kernelIDF16bLi128ELb1E", "_ZN2fa14bwd_pre_kernelIDF16bLi128E"
+    dkdv, dq = "_ZN2fa13dkdv16_kernelIDF16bLi128ELb1E", "_ZN2fa11dq16_kernelIDF16bLi128ELb1E"
+    other = "_ZN2fa12fwd16_kernelIDF16_Li64ELb0E"
+    warmup, steps = 1, 3
+    seq = []
+    for s in range(warmup + steps):
+        slow = 10.0 if s < warmup else 0.0   # warm-up dispatches are slower and must be left out
+        seq += [(fwd, 100 + slow), (pre, 10 + slow), (dkdv, 300 + s + slow), (dq, 200 + slow)]
+    seq += [(other, 1000.0)] * 30 + [(fwd, 5000.0)] * 5   # forward-only lines timed after the step
+    _write_trace(str(tmp_path / "trace"), seq)
+    bench.write_trace_summary(str(tmp_path / "trace"), W.WORKLOADS["c5"], warmup, steps, out_dir=str(tmp_path))
+    text = (tmp_path / "c5_step_kernel_stats.md").read_text()
+    rows = {line.split("|")[1].strip(): line.split("|") for line in text.splitlines()
+            if line.startswith("| fa_")}
+    assert set(rows) == {"fa_fwd", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq"}
+    assert other not in text.split("All dispatches")[0]
+    assert float(rows["fa_bwd_dkdv"][3]) == pytest.approx(301 + 1.0, abs=0.05)   # mean of 301, 302, 303
+    assert float(rows["fa_fwd"][3]) == pytest.approx(100.0, abs=0.05)
+    assert "Step (sum of the kernels' averages): 612.0 us" in text
