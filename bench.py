@@ -58,9 +58,10 @@ def kernel_models(w):
     r = 4.0 * n * bh            # one fp32 [B,H,N] vector
     return {
         "fwd": {"flops": 4 * nn, "bytes": 3 * t + t + r},
-        "bwd_rowsum": {"flops": 2.0 * n * d * bh, "bytes": 2 * t + r},
+        # dQ, first backward stage: reads q, k, v, o, dout and lse, writes dq and the row sums D
+        "bwd_dq": {"flops": 2 * nn, "bytes": 5 * t + r + t + r},
+        # dK/dV: reads q, k, v, dout, lse and D, writes dk and dv
         "bwd_dkdv": {"flops": 8 * nn, "bytes": 4 * t + 2 * r + 2 * t},
-        "bwd_dq": {"flops": 2 * nn, "bytes": 4 * t + 2 * r + t},
     }
 
 
@@ -85,8 +86,7 @@ def traffic_for(kernel):
     return entry.get("hbm_bytes_per_launch")
 
 
-STEP_KERNELS = {"fwd16_kernel": "fwd", "bwd_pre_kernel": "bwd_rowsum", "dkdv16_kernel": "bwd_dkdv",
-                "dq16_kernel": "bwd_dq"}
+STEP_KERNELS = {"fwd16_kernel": "fwd", "dkdv16_kernel": "bwd_dkdv", "dq16_kernel": "bwd_dq"}
 
 
 # --------------------------------------------------------------- counter reports
@@ -251,7 +251,7 @@ def write_counter_report(prof_dir, w, cal_dir):
     return rep
 
 
-STEP_LABELS = {"fwd": "fa_fwd", "bwd_rowsum": "fa_bwd_rowsum", "bwd_dkdv": "fa_bwd_dkdv", "bwd_dq": "fa_bwd_dq"}
+STEP_LABELS = {"fwd": "fa_fwd", "bwd_dq": "fa_bwd_dq_rowsum", "bwd_dkdv": "fa_bwd_dkdv"}
 
 
 def write_trace_summary(trace_dir, w, warmup, steps, bench_log=None, out_dir=None):
@@ -466,9 +466,12 @@ class Runner:
                                 self.lse.data_ptr(), *self.dims, w.scale, int(w.causal), self.code, self.stream),
                  "fa_fwd")
 
-    def rowsum(self):
-        self._ok(self.fa.fa_bwd_rowsum(self.o.data_ptr(), self.do.data_ptr(), self.ws.data_ptr(), self.wsb,
-                                       *self.dims, self.code, self.stream), "fa_bwd_rowsum")
+    def dq_rowsum(self):
+        w = self.w
+        self._ok(self.fa.fa_bwd_dq_rowsum(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                          self.o.data_ptr(), self.do.data_ptr(), self.lse.data_ptr(),
+                                          self.ws.data_ptr(), self.wsb, self.dq.data_ptr(), *self.dims, w.scale,
+                                          int(w.causal), self.code, self.stream), "fa_bwd_dq_rowsum")
 
     def dkdv(self):
         w = self.w
@@ -477,11 +480,6 @@ class Runner:
                                      self.dv.data_ptr(), *self.dims, w.scale, int(w.causal), self.code,
                                      self.stream), "fa_bwd_dkdv")
 
-    def dq_(self):
-        w = self.w
-        self._ok(self.fa.fa_bwd_dq(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.do.data_ptr(),
-                                   self.lse.data_ptr(), self.ws.data_ptr(), self.wsb, self.dq.data_ptr(),
-                                   *self.dims, w.scale, int(w.causal), self.code, self.stream), "fa_bwd_dq")
 
 
 def _spread(times_ms):
@@ -683,7 +681,8 @@ def main():
         raise SystemExit(f"workload {w.name} has no backward; the step needs fwd+bwd")
     log(f"bench: workload {w.name} {w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
     r = Runner(w, dev)
-    stages = [("fwd", r.fwd), ("bwd_rowsum", r.rowsum), ("bwd_dkdv", r.dkdv), ("bwd_dq", r.dq_)]
+    # fa_bwd's own sequence: dQ (forming the row sums D on the way), then dK/dV
+    stages = [("fwd", r.fwd), ("bwd_dq", r.dq_rowsum), ("bwd_dkdv", r.dkdv)]
 
     for _ in range(args.warmup):
         for _, f in stages:

@@ -18,7 +18,7 @@ import math
 import os
 
 __all__ = ["FA_F32", "FA_F16", "FA_BF16", "FaError", "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes",
-           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
+           "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_rowsum", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse",
            "fa_bwd_sparse", "fa_status_string", "fa_version", "forward", "backward", "forward_kv",
            "backward_kv", "forward_sparse", "backward_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "forward_dropout", "backward_dropout", "fa_fwd_fp8", "fa_fwd_fp8_fmt", "forward_fp8", "fa_fwd_kv_split",
@@ -38,7 +38,7 @@ _LIB = None
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_rowsum", "fa_bwd_dkdv", "fa_bwd_dq",
            "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_fwd_fp8", "fa_fwd_fp8_fmt", "fa_fwd_kv_split", "fa_fwd_kv_split_workspace_bytes",
-           "fa_fwd_kv_split_hint", "fa_bwd_static", "fa_status_string", "fa_version")
+           "fa_fwd_kv_split_hint", "fa_bwd_static", "fa_bwd_dq_rowsum", "fa_status_string", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -75,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, i, vp]
     lib.fa_bwd_dq.restype = i
+    lib.fa_bwd_dq_rowsum.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd_dq_rowsum.restype = i
     lib.fa_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, f, i, i, vp]
     lib.fa_fwd_kv.restype = i
     lib.fa_bwd_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, vp, vp, f, i, i, vp]
@@ -136,6 +138,12 @@ def fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, sc
               stream) -> int:
     return load().fa_bwd_dq(q, k, v, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, scale, causal,
                             dtype, stream)
+
+
+def fa_bwd_dq_rowsum(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, scale, causal, dtype,
+                     stream) -> int:
+    return load().fa_bwd_dq_rowsum(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, B, H, N, d, scale,
+                                   causal, dtype, stream)
 
 
 def fa_fwd_kv(q, k, v, o, lse, B, H, Nq, Nk, d, seqlens_q, seqlens_k, scale, causal, dtype, stream) -> int:

@@ -6,6 +6,7 @@
 // caller's stream.  No device memory is allocated, freed or cached here.
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -301,15 +302,22 @@ fa::BwdProblem bwd_problem(const BwdPtrs& p, int B, int H, int Nq, int Nk, int d
   b.drop_on = drop.on; b.drop_threshold = drop.threshold; b.drop_seed_lo = drop.seed_lo;
   b.drop_seed_hi = drop.seed_hi; b.drop_offset = drop.offset; b.drop_scale = drop.scale;
   b.scale = scale; b.causal = causal; b.dtype = dtype;
+  b.dq_rowsum = 0;
   return b;
 }
 
-int run_stages(const fa::BwdProblem& b, int first, int last, void* stream) {
+int run_stages(const fa::BwdProblem& b, std::initializer_list<int> stages, void* stream) {
   (void)hipGetLastError();  // report only these launches' errors
   hipError_t e = hipSuccess;
-  for (int s = first; s <= last && e == hipSuccess; ++s) e = fa::launch_bwd_stage(b, s, reinterpret_cast<hipStream_t>(stream));
+  for (int s : stages) {
+    e = fa::launch_bwd_stage(b, s, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) break;
+  }
   return hip_status(e);
 }
+
+// A whole backward pass: dQ with the row sums D formed on the way, then dK/dV.
+int run_bwd(const fa::BwdProblem& b, void* stream) { return run_stages(b, {3, 1}, stream); }
 
 }  // namespace
 
@@ -321,7 +329,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
   int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), 0, 2, stream);
+  return run_bwd(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), stream);
 }
 
 int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -331,8 +339,7 @@ int fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const 
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
   int st = check_bwd(p, workspace_bytes, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype), 0, 2,
-                    stream);
+  return run_bwd(bwd_problem(p, B, H, Nq, Nk, d, seqlens_q, seqlens_k, nullptr, scale, causal, (int)dtype), stream);
 }
 
 int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -343,8 +350,7 @@ int fa_bwd_sparse(const void* q, const void* k, const void* v, const void* o, co
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
   int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype), 0, 2,
-                    stream);
+  return run_bwd(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, block_mask, scale, causal, (int)dtype), stream);
 }
 
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -357,8 +363,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   const BwdPtrs p{q, k, v, o, dout, lse, dq, dk, dv, workspace};
   st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, drop), 0, 2,
-                    stream);
+  return run_bwd(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype, drop), stream);
 }
 
 int fa_bwd_static(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -373,7 +378,7 @@ int fa_bwd_static(const void* q, const void* k, const void* v, const void* o, co
   if (fa::static_scratch(reinterpret_cast<hipStream_t>(stream), &dvec) != hipSuccess) return FA_ERR_HIP;
   fa::BwdProblem b = bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   b.dvec = dvec;
-  return run_stages(b, 0, 2, stream);
+  return run_bwd(b, stream);
 }
 
 int fa_bwd_rowsum(const void* o, const void* dout, void* workspace, size_t workspace_bytes, int B, int H, int N,
@@ -382,7 +387,7 @@ int fa_bwd_rowsum(const void* o, const void* dout, void* workspace, size_t works
   const BwdPtrs p{kUnused, kUnused, kUnused, o, dout, kUnused, un, un, un, workspace};
   int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, 1.0f, 0, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, 1.0f, 0, (int)dtype), 0, 0, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, 1.0f, 0, (int)dtype), {0}, stream);
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -392,7 +397,17 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, c
   const BwdPtrs p{q, k, v, kUnused, dout, lse, un, dk, dv, const_cast<void*>(workspace)};
   int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), 1, 1, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), {1}, stream);
+}
+
+int fa_bwd_dq_rowsum(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* workspace, size_t workspace_bytes, void* dq, int B, int H, int N, int d, float scale,
+                     int causal, fa_dtype dtype, void* stream) {
+  void* un = const_cast<void*>(kUnused);
+  const BwdPtrs p{q, k, v, o, dout, lse, dq, un, un, workspace};
+  int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
+  if (st != FA_OK) return st;
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), {3}, stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, const void* workspace,
@@ -402,7 +417,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, con
   const BwdPtrs p{q, k, v, kUnused, dout, lse, dq, un, un, const_cast<void*>(workspace)};
   int st = check_bwd(p, workspace_bytes, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype);
   if (st != FA_OK) return st;
-  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), 2, 2, stream);
+  return run_stages(bwd_problem(p, B, H, N, N, d, nullptr, nullptr, nullptr, scale, causal, (int)dtype), {2}, stream);
 }
 
 }  // extern "C"

@@ -567,6 +567,15 @@ static hipError_t launch_bwd_s(const BwdProblem& p, int stage, hipStream_t s) {
 // rejects that.)
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s) {
   if (stage == 0) return launch_pre(p, s);
+  if (stage == 3) {
+    if (p.dtype != 0) {  // the 16-bit dQ kernel forms D from its own dO rows and the O rows
+      BwdProblem f = p;
+      f.dq_rowsum = 1;
+      return launch_dq16(f, s);
+    }
+    const hipError_t e = launch_pre(p, s);
+    return e != hipSuccess ? e : launch_bwd_stage(p, 2, s);
+  }
   if (p.dtype != 0) return stage == 1 ? launch_dkdv16(p, s) : launch_dq16(p, s);
   if (p.drop_on) return launch_bwd_s<float, false, true>(p, stage, s);
   return p.block_mask != nullptr ? launch_bwd_s<float, true, false>(p, stage, s)

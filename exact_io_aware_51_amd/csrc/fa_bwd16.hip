@@ -26,6 +26,8 @@ struct Bwd16Args {
   const void* dout;
   const float* lse;
   const float* dvec;
+  const void* o;     // dQ kernel: non-null = form D from o and dout and write it to dvec_out
+  float* dvec_out;
   void* dq;
   void* dk;
   void* dv;
@@ -63,7 +65,9 @@ __device__ inline void reads_ahead() {
 // streams 64-key K/V tiles.  Step j computes S^T_j = K_j Q^T and
 // dP^T_j = V_j dO^T, then forms dS^T_j while the matrix cores accumulate
 // dQ^T += K_{j-1}^T dS^T_{j-1}.  LDS: K in three stages (K_{j-1}, K_j and the
-// one being loaded), V in two.
+// one being loaded), V in two.  Launched as the first backward stage, the
+// kernel also forms the row sums D of its queries (it holds their dO rows
+// already) and writes them for the dK/dV kernel.
 // dQ kernel, dense d = 128 (no dropout, no block mask): two waves per SIMD
 // (256 VGPRs each) with each tile's dQ products issued in its own step and no
 // extra read-ahead schedule.  Carrying dS into the next step (the schedule of
@@ -85,10 +89,16 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
   using Frag = typename M::Frag;
   constexpr int KSTEPS = D / 16;
   constexpr int MB = D / 32;
-  constexpr int KREG = 0;                // [K0 K1 K2 V0 V1]
-  constexpr int VREG = 3 * TL::BYTES;
+  // K stages: three when tile j-1's dQ products run in step j (K_{j-1}, K_j
+  // and the one being loaded), two when each tile's dQ products finish in its
+  // own step; V always two.  With two K stages every LDS offset of a step fits
+  // a read instruction's 16-bit immediate at d = 128, which saves the address
+  // registers that V's second stage would otherwise need.
+  constexpr int KST = NOPIPE ? 2 : 3;
+  constexpr int KREG = 0;                // [K0 K1 (K2) V0 V1]
+  constexpr int VREG = KST * TL::BYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[5 * TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[(KST + 2) * TL::BYTES];
 
   const int tid = thread_id();
   const int lane = tid & 63;
@@ -116,7 +126,26 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
     dof[ks] = myq < sq.lq ? row_frag<T>(dO + (size_t)myq * D + ks * 16, h) : zero_frag<T>();
   }
   const float lse2 = myq < sq.lq ? a.lse[(size_t)bh * Nq + myq] * kLog2e : 0.0f;
-  const float dd = myq < sq.lq ? a.dvec[(size_t)bh * Nq + myq] : 0.0f;
+  float dd;
+  if (a.o != nullptr) {
+    // D = rowsum(dO o O) of the lane's query from its dO fragments and the
+    // matching halves of its O row (the two half-waves hold the two halves),
+    // written for the dK/dV kernel that runs after this one
+    float part = 0.0f;
+    if (myq < sq.lq) {
+      const T* O = reinterpret_cast<const T*>(a.o) + headq + (size_t)myq * D;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const Frag of = row_frag<T>(O + ks * 16, h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)of[e], (float)dof[ks][e], part);
+      }
+    }
+    dd = halves_sum(part);
+    if (h == 0 && myq < Nq) a.dvec_out[(size_t)bh * Nq + myq] = dd;
+  } else {
+    dd = myq < sq.lq ? a.dvec[(size_t)bh * Nq + myq] : 0.0f;
+  }
 
   // key tiles this block visits, and how many leading ones no real row sees masked
   int nt, nt_full;
@@ -176,11 +205,11 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
   // K_jp in the K stage before ks3.  Stages advance by one per step.
   auto step = [&](int j, int jn, int jp, auto ks3, auto vs2, auto full_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
-    const int kps = ks3 == 0 ? 2 : ks3 - 1;
+    const int kps = ks3 == 0 ? KST - 1 : ks3 - 1;
     wait_vmem();
     __builtin_amdgcn_s_barrier();
     if (jn < nt) {
-      const int kn = ks3 == 2 ? 0 : ks3 + 1;
+      const int kn = ks3 == KST - 1 ? 0 : ks3 + 1;
       dma(Kg, 64 * jn, KREG + kn * TL::BYTES);
       dma(Vg, 64 * jn, VREG + (vs2 ^ 1) * TL::BYTES);
     }
@@ -247,28 +276,33 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
       // dropout) take the runtime-stage loop below, which keeps one register
       // assignment for the accumulators and lets the LDS reads run ahead.
       constexpr bool UNROLL6 = DqShape<D, SPARSE, DROP>::OCC == 2;
+      // (j starts at 1: K stages j % KST = 1, 2, 0, 1, 2, 0 or 1, 0, 1, 0, 1, 0)
+      using K2 = std::conditional_t<KST == 2, I0, I2>;
+      using K0 = std::conditional_t<KST == 2, I1, I0>;
+      using K1 = std::conditional_t<KST == 2, I0, I1>;
+      using K2b = std::conditional_t<KST == 2, I1, I2>;
       for (; UNROLL6 && j + 5 < nt_full; j += 6) {
         step(j, j + 1, j - 1, I1{}, I1{}, std::true_type{});
-        step(j + 1, j + 2, j, I2{}, I0{}, std::true_type{});
-        step(j + 2, j + 3, j + 1, I0{}, I1{}, std::true_type{});
-        step(j + 3, j + 4, j + 2, I1{}, I0{}, std::true_type{});
-        step(j + 4, j + 5, j + 3, I2{}, I1{}, std::true_type{});
+        step(j + 1, j + 2, j, K2{}, I0{}, std::true_type{});
+        step(j + 2, j + 3, j + 1, K0{}, I1{}, std::true_type{});
+        step(j + 3, j + 4, j + 2, K1{}, I0{}, std::true_type{});
+        step(j + 4, j + 5, j + 3, K2b{}, I1{}, std::true_type{});
         step(j + 5, j + 6, j + 4, I0{}, I0{}, std::true_type{});
       }
       // the rest (up to five mask-free tiles, then the masked ones): runtime stages
       for (; j < nt; ++j) {
         if (j < nt_full)
-          step(j, j + 1, j - 1, j % 3, j & 1, std::true_type{});
+          step(j, j + 1, j - 1, j % KST, j & 1, std::true_type{});
         else
-          step(j, j + 1, j - 1, j % 3, j & 1, std::false_type{});
+          step(j, j + 1, j - 1, j % KST, j & 1, std::false_type{});
       }
       wait_vmem();
       __builtin_amdgcn_s_barrier();
-      if (!NOPIPE && (!CAUSAL || 64 * (nt - 1) <= wlast)) dq_prev((nt - 1) % 3);
+      if (!NOPIPE && (!CAUSAL || 64 * (nt - 1) <= wlast)) dq_prev((nt - 1) % KST);
     }
   } else {
     // Only live tiles are visited, in increasing order; step t uses K stage
-    // t % 3 and V stage t % 2, and is unmasked when its tile lies below nt_full.
+    // t % KST and V stage t % 2, and is unmasked when its tile lies below nt_full.
     auto next = [&](int j) __attribute__((always_inline)) { return next_live_tile(mwords, j, 2, a.nbk, nt); };
     int j = next(-1);
     if (j < nt) {
@@ -282,19 +316,19 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
       // that no loop holds both step bodies
       for (; j < nt_full; ++t) {
         jn = next(j);
-        step(j, jn, jp, t % 3, t & 1, std::true_type{});
+        step(j, jn, jp, t % KST, t & 1, std::true_type{});
         jp = j;
         j = jn;
       }
       for (; j < nt; ++t) {
         jn = next(j);
-        step(j, jn, jp, t % 3, t & 1, std::false_type{});
+        step(j, jn, jp, t % KST, t & 1, std::false_type{});
         jp = j;
         j = jn;
       }
       wait_vmem();
       __builtin_amdgcn_s_barrier();
-      if (!NOPIPE && (!CAUSAL || 64 * jp <= wlast)) dq_prev((t - 1) % 3);
+      if (!NOPIPE && (!CAUSAL || 64 * jp <= wlast)) dq_prev((t - 1) % KST);
     }
   }
 
@@ -572,6 +606,8 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
 static Bwd16Args bwd16_args(const BwdProblem& p, int nblk) {
   Bwd16Args a;
   a.q = p.q; a.k = p.k; a.v = p.v; a.dout = p.dout; a.lse = p.lse; a.dvec = p.dvec;
+  a.o = p.dq_rowsum ? p.o : nullptr;
+  a.dvec_out = p.dq_rowsum ? p.dvec : nullptr;
   a.dq = p.dq; a.dk = p.dk; a.dv = p.dv;
   a.seqlens_q = p.seqlens_q; a.seqlens_k = p.seqlens_k;
   a.block_mask = p.block_mask;

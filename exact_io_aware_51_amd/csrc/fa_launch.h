@@ -60,6 +60,9 @@ struct BwdProblem {
   float scale;
   int causal;
   int dtype;
+  // launch_dq16 only: the dQ kernel also forms D from o and dout and writes it
+  // to dvec, for the dK/dV stage that runs after it (no row-sum stage)
+  int dq_rowsum;
 };
 
 hipError_t launch_fwd(const FwdProblem& p, hipStream_t s);
@@ -75,7 +78,8 @@ constexpr long long kStaticScratchRows = 1LL << 22;
 // That scratch's address on the device `stream` runs on (looked up once per
 // device; allocates nothing).
 hipError_t static_scratch(hipStream_t stream, float** out);
-// stage: 0 = row sums D, 1 = dK/dV, 2 = dQ
+// stage: 0 = row sums D, 1 = dK/dV (reads D), 2 = dQ (reads D), 3 = dQ that
+// forms and writes D itself (so the sequence 3, 1 is a whole backward pass)
 hipError_t launch_bwd_stage(const BwdProblem& p, int stage, hipStream_t s);
 hipError_t launch_dq16(const BwdProblem& p, hipStream_t s);    // bf16 / fp16 only
 hipError_t launch_dkdv16(const BwdProblem& p, hipStream_t s);  // bf16 / fp16 only

@@ -102,16 +102,22 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o,
            fa_dtype dtype, void *stream);
 
 /*
- * The three stages fa_bwd queues, for callers that schedule them themselves
+ * The stages of the backward pass, for callers that schedule them themselves
  * (for instance dK/dV and dQ on two streams once the row sums are done, or
  * timing each stage).  fa_bwd(...) is exactly
- *     fa_bwd_rowsum(...); fa_bwd_dkdv(...); fa_bwd_dq(...);
- * on one stream.  Arguments mean what they mean for fa_bwd; each stage
- * validates the arguments it uses.  The workspace carries D from
- * fa_bwd_rowsum to the other two stages, so it must not be reused in between.
- *   fa_bwd_rowsum : workspace <- D_i = sum_c dout_ic * o_ic (fp32)
- *   fa_bwd_dkdv   : dk, dv   (reads q, k, v, dout, lse, workspace)
- *   fa_bwd_dq     : dq       (reads q, k, v, dout, lse, workspace)
+ *     fa_bwd_dq_rowsum(...); fa_bwd_dkdv(...);
+ * on one stream: the dQ stage forms the row sums D on the way (it holds each
+ * query's dout row already, so D costs one read of o and no launch of its
+ * own) and leaves them in the workspace for the dK/dV stage.  The same
+ * result, up to the summation order of D, comes from
+ *     fa_bwd_rowsum(...); then fa_bwd_dkdv(...) and fa_bwd_dq(...) in any order.
+ * Arguments mean what they mean for fa_bwd; each stage validates the
+ * arguments it uses.  The workspace carries D between stages, so it must not
+ * be reused in between.
+ *   fa_bwd_rowsum    : workspace <- D_i = sum_c dout_ic * o_ic (fp32)
+ *   fa_bwd_dq_rowsum : dq, and workspace <- D (reads q, k, v, o, dout, lse)
+ *   fa_bwd_dkdv      : dk, dv   (reads q, k, v, dout, lse, workspace)
+ *   fa_bwd_dq        : dq       (reads q, k, v, dout, lse, workspace)
  */
 int fa_bwd_rowsum(const void *o, const void *dout, void *workspace, size_t workspace_bytes,
                   int B, int H, int N, int d, fa_dtype dtype, void *stream);
@@ -121,6 +127,9 @@ int fa_bwd_dkdv(const void *q, const void *k, const void *v, const void *dout, c
 int fa_bwd_dq(const void *q, const void *k, const void *v, const void *dout, const float *lse,
               const void *workspace, size_t workspace_bytes, void *dq,
               int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
+int fa_bwd_dq_rowsum(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, void *workspace, size_t workspace_bytes, void *dq,
+                     int B, int H, int N, int d, float scale, int causal, fa_dtype dtype, void *stream);
 
 /*
  * fa_bwd for callers that cannot allocate device memory (code under HIP graph

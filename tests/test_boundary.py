@@ -42,7 +42,8 @@ def test_header_declares_the_abi():
                                   "fa_bwd_dq", "fa_fwd_kv", "fa_bwd_kv", "fa_fwd_sparse", "fa_bwd_sparse",
                                   "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_fp8", "fa_fwd_kv_split",
                                   "fa_fwd_kv_split_workspace_bytes", "fa_fwd_kv_split_hint", "fa_status_string",
-                                  "fa_version", "fa_bwd_static", "fa_fwd_fp8_fmt"])
+                                  "fa_version", "fa_bwd_static", "fa_fwd_fp8_fmt",
+                                  "fa_bwd_dq_rowsum"])
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -171,7 +172,25 @@ STAGE_BAD = [
     ("dq misaligned dq", lambda fa: fa.fa_bwd_dq(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), _ptr(9), 1 << 20, _ptr(6, 8), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -1),
     ("dq no workspace", lambda fa: fa.fa_bwd_dq(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), None, 1 << 20, _ptr(6), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -3),
     ("dq aliases k", lambda fa: fa.fa_bwd_dq(_ptr(0), _ptr(1), _ptr(2), _ptr(4), _ptr(5), _ptr(9), 1 << 20, _ptr(1), 1, 2, 256, 64, 0.125, 1, fa.FA_BF16, None), -1),
+    # the dQ stage that also writes the row sums: o is read, the workspace written
+    ("dq_rowsum null o", lambda fa: _dq_rowsum(fa, o=None), -1),
+    ("dq_rowsum misaligned o", lambda fa: _dq_rowsum(fa, o=_ptr(3, 8)), -1),
+    ("dq_rowsum no workspace", lambda fa: _dq_rowsum(fa, ws=None), -3),
+    ("dq_rowsum small workspace", lambda fa: _dq_rowsum(fa, wsb=64), -3),
+    ("dq_rowsum workspace aliases o", lambda fa: _dq_rowsum(fa, ws=_ptr(3)), -3),
+    ("dq_rowsum dq aliases o", lambda fa: _dq_rowsum(fa, dq=_ptr(3)), -1),
+    ("dq_rowsum dq aliases workspace", lambda fa: _dq_rowsum(fa, dq=_ptr(9)), -3),
+    ("dq_rowsum d=96", lambda fa: _dq_rowsum(fa, d=96), -2),
+    ("dq_rowsum causal=3", lambda fa: _dq_rowsum(fa, causal=3), -1),
 ]
+
+
+def _dq_rowsum(fa, **kw):
+    a = dict(q=_ptr(0), k=_ptr(1), v=_ptr(2), o=_ptr(3), do=_ptr(4), lse=_ptr(5), ws=_ptr(9), wsb=1 << 20,
+             dq=_ptr(6), B=1, H=2, N=256, d=64, scale=0.125, causal=1, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fa_bwd_dq_rowsum(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["ws"], a["wsb"], a["dq"],
+                               a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
 
 
 @pytest.mark.parametrize("name,call,want", STAGE_BAD, ids=[x[0] for x in STAGE_BAD])
@@ -393,6 +412,8 @@ def test_valid_call_without_device_reports_hip_error(fa):
     assert _bwd_static(fa) == fa.FA_ERR_HIP
     assert _bwd_static(fa, B=1, H=1, N=1 << 22) == fa.FA_ERR_HIP  # exactly the capacity is accepted
     assert fa.fa_bwd_rowsum(_ptr(3), _ptr(4), _ptr(9), 1 << 20, 1, 2, 256, 64, fa.FA_BF16, None) == fa.FA_ERR_HIP
+    assert _dq_rowsum(fa) == fa.FA_ERR_HIP
+    assert _dq_rowsum(fa, dtype=fa.FA_F32, causal=0, d=128) == fa.FA_ERR_HIP
     assert _fwd_kv(fa) == fa.FA_ERR_HIP
     assert _fwd_kv(fa, sq=None, sk=None, Nq=1) == fa.FA_ERR_HIP
     assert _bwd_kv(fa) == fa.FA_ERR_HIP
