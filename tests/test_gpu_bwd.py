@@ -102,3 +102,57 @@ def test_bwd_large_scale_within_rounding_model(scale, dtype):
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         rel = np.linalg.norm(g - r) / np.linalg.norm(r)
         assert rel <= GRAD_REL[dtype], f"{name}: relative Frobenius error {rel:.3e} > {GRAD_REL[dtype]:.0e}"
+
+
+def _stage_call(fa, name, args):
+    st = getattr(fa, name)(*args)
+    assert st == fa.FA_OK, f"{name}: {fa.fa_status_string(st)}"
+
+
+@pytest.mark.parametrize("dtype,causal,shape", [("bf16", True, (1, 2, 300, 128)), ("f16", False, (2, 1, 257, 64)),
+                                                ("bf16", False, (1, 3, 1000, 128)), ("f32", True, (1, 2, 129, 64))],
+                         ids=["bf16-causal-300x128", "f16-full-257x64", "bf16-full-1000x128", "f32-causal-129x64"])
+def test_bwd_stage_entry_points(dtype, causal, shape):
+    """fa_bwd is fa_bwd_dq_rowsum then fa_bwd_dkdv (bit for bit); the three-launch
+    sequence fa_bwd_rowsum, fa_bwd_dkdv, fa_bwd_dq gives the same gradients up to
+    D's summation order and passes the oracle's gates; both row sums match
+    sum_c dO_ic O_ic of the stored O within fp32 rounding."""
+    import exact_io_aware_51_amd as fa
+    dev = device()
+    B, H, N, d = shape
+    w = W.shape_case(B, H, N, d, dtype, causal, seed=53 + N + d)
+    announce("bwd stages", w.name)
+    q, k, v, do = to_dev(W.make_inputs(w), dev)
+    o, lse = fa.forward(q, k, v, scale=w.scale, causal=causal)
+    ref_dq, ref_dk, ref_dv = fa.backward(q, k, v, o, lse, do, scale=w.scale, causal=causal)
+    code = {"bf16": fa.FA_BF16, "f16": fa.FA_F16, "f32": fa.FA_F32}[dtype]
+    wsb = fa.fa_bwd_workspace_bytes(B, H, N, d, code)
+    stream = torch.cuda.current_stream().cuda_stream
+    sd = (B, H, N, d, w.scale, int(causal), code, stream)
+    p = lambda t: t.data_ptr()  # noqa: E731
+
+    ws1 = torch.full((wsb,), 0xFF, dtype=torch.uint8, device=dev)  # garbage D: the stage must overwrite it
+    dq1, dk1, dv1 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _stage_call(fa, "fa_bwd_dq_rowsum", (p(q), p(k), p(v), p(o), p(do), p(lse), p(ws1), wsb, p(dq1), *sd))
+    _stage_call(fa, "fa_bwd_dkdv", (p(q), p(k), p(v), p(do), p(lse), p(ws1), wsb, p(dk1), p(dv1), *sd))
+
+    ws2 = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+    dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _stage_call(fa, "fa_bwd_rowsum", (p(o), p(do), p(ws2), wsb, B, H, N, d, code, stream))
+    _stage_call(fa, "fa_bwd_dkdv", (p(q), p(k), p(v), p(do), p(lse), p(ws2), wsb, p(dk2), p(dv2), *sd))
+    _stage_call(fa, "fa_bwd_dq", (p(q), p(k), p(v), p(do), p(lse), p(ws2), wsb, p(dq2), *sd))
+    torch.cuda.synchronize()
+
+    for a, b, what in zip((dq1, dk1, dv1), (ref_dq, ref_dk, ref_dv), ("dQ", "dK", "dV")):
+        assert torch.equal(a, b), f"{what}: fa_bwd_dq_rowsum + fa_bwd_dkdv differ from fa_bwd"
+    rows = B * H * N
+    d1 = ws1[:rows * 4].view(torch.float32).double().cpu().numpy()
+    d2 = ws2[:rows * 4].view(torch.float32).double().cpu().numpy()
+    prod = (to_np(do) * to_np(o)).reshape(rows, d)
+    exact, mag = prod.sum(axis=1), np.abs(prod).sum(axis=1)
+    tol = d * 2.0 ** -24 * mag + 1e-30   # fp32 sums of d exact products, any order
+    assert np.all(np.abs(d1 - exact) <= tol), "row sums from the dQ stage"
+    assert np.all(np.abs(d2 - exact) <= tol), "row sums from fa_bwd_rowsum"
+    ref = oracle.attention_backward(*(t.cpu() for t in (q, k, v, do)), w.scale, causal)
+    for got, what in (((dq1, dk1, dv1), "two-stage"), ((dq2, dk2, dv2), "three-stage")):
+        _check_grads(got, ref, dtype, f"{w.name} {what}")
