@@ -601,6 +601,233 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
   }
 }
 
+// --------------------------------------------------------------------------
+// dK, dV at d = 128 without dropout, a block mask or the causal mask (under
+// the causal mask the 32-key kernel measured 1-2% faster on long rows, and
+// runs there): a workgroup of eight
+// waves owns 128 keys, 16 per wave, so that two waves share each SIMD.  With
+// 32 keys per wave (dkdv16_kernel) the dK/dV accumulators and the stationary
+// K/V fragments alone take 192 registers and the kernel runs one wave per
+// SIMD; with 16 keys they take 96.  The products run on the 16x16x32
+// instruction (the same rate per flop).  Per 32-query half and wave:
+// S = Q K^T and dP = dO V^T (two 16-query blocks, four 32-channel steps),
+// then dV^T += dO^T P and dK^T += Q^T dS (eight 16-channel blocks, the 32
+// queries as one contraction step).  P and dS go from the accumulators
+// straight into the B operand: a lane holds its key's weights for queries
+// 16 b + 4 g + r (g = lane / 16, b = query block, r = register), which become
+// contraction slot 8 g + 4 b + r, and the transposing reads of dO and Q hand
+// the A operand the same queries in the same slots.  The Q and dO tiles keep
+// their 16-byte chunks permuted by Tile16n::sw, under which both read
+// patterns are conflict-free: 16 lanes reading one chunk of 16 consecutive
+// rows, and 32 lanes reading two adjacent chunks of 8 consecutive rows.
+// Operand reads kept in flight ahead of the 16x16x32 products: row fragments
+// of S / dP, and transposing pairs of dV / dK.
+constexpr int kNarrowRowAhead = 8;
+constexpr int kNarrowTrAhead = 4;
+
+struct Tile16n {
+  static constexpr int ROWB = 256;    // one row of 128 16-bit values
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int ROUNDS = 2;    // direct loads per tile and wave (eight waves)
+  __device__ static constexpr int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+  __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
+};
+
+template <typename T>
+__global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
+  using M = Mma16<T>;
+  using Frag = typename M::Frag;
+  using TL = Tile16n;
+  constexpr int D = 128;
+  constexpr int KS = D / 32;             // contraction steps of S and dP
+  constexpr int NB = D / 16;             // 16-channel blocks of dK^T and dV^T
+  constexpr int QREG = 0;                // [Q0 Q1 dO0 dO1 lse0 lse1 D0 D1]
+  constexpr int OREG = 2 * TL::BYTES;
+  constexpr int LREG = 4 * TL::BYTES;    // 2 x 64 floats of -LSE * log2(e)
+  constexpr int DREG = LREG + 512;       // 2 x 64 floats of D
+
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TL::BYTES + 1024];
+
+  const int tid = thread_id();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, col = lane & 15;
+  const int Nq = a.Nq, Nk = a.Nk;
+
+  int bh, kblk;
+  block_order<32>(block_id(), a.total, a.nblk, false, &bh, &kblk);
+  const int kb0 = kblk * 128;
+  const int kw = kb0 + 16 * wave;
+  const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
+  const size_t headq = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
+  const char* Qg = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.q) + headq);
+  const char* Og = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.dout) + headq);
+  const float* lse = a.lse + (size_t)bh * Nq;
+  const float* dvec = a.dvec + (size_t)bh * Nq;
+
+  // B operands of S and dP: the lane's key, channels 32 ks + 8 g .. + 7
+  const int mykey = kw + col;
+  Frag kf[KS], vf[KS];
+  {
+    const T* Kp = reinterpret_cast<const T*>(a.k) + headk + (size_t)mykey * D + 8 * g;
+    const T* Vp = reinterpret_cast<const T*>(a.v) + headk + (size_t)mykey * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = mykey < sq.lk ? __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(Kp + 32 * ks)) : zero_frag<T>();
+      vf[ks] = mykey < sq.lk ? __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(Vp + 32 * ks)) : zero_frag<T>();
+    }
+  }
+
+  // query tiles of real queries (a block of padding keys visits none); the
+  // last one is ragged unless lq is a multiple of 64
+  const int nt = kb0 < sq.lk ? (sq.lq + 63) / 64 : 0;
+  const int full1 = sq.lq / 64;
+
+  // direct loads: slot s = (8 r + wave) * 64 + lane, 16 bytes at LDS byte 16 s,
+  // holds logical chunk (s % 16) ^ sw(row) of row s / 16
+  uint32_t goff[TL::ROUNDS];
+#pragma unroll
+  for (int r = 0; r < TL::ROUNDS; ++r) {
+    const int sl = (r * 8 + wave) * 64 + lane;
+    const int row = sl >> 4, pc = sl & 15;
+    goff[r] = row * TL::ROWB + ((pc ^ TL::sw(row)) << 4);
+  }
+  float lse_next = 0.0f, d_next = 0.0f;  // wave 0 stages the next tile's per-row values
+  auto fetch = [&](int i, int stage) __attribute__((always_inline)) {
+    const int row0 = 64 * i;
+    const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, tile_bytes(sq.lq - row0, 64, TL::ROWB));
+    const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, tile_bytes(sq.lq - row0, 64, TL::ROWB));
+#pragma unroll
+    for (int r = 0; r < TL::ROUNDS; ++r) {
+      lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * 8 + wave) * 1024, goff[r]);
+      lds_load16(ro, smem + OREG + stage * TL::BYTES + (r * 8 + wave) * 1024, goff[r]);
+    }
+    if (wave == 0) {
+      const int qi = row0 + lane;
+      lse_next = qi < sq.lq ? -lse[qi] * kLog2e : 0.0f;
+      d_next = qi < sq.lq ? dvec[qi] : 0.0f;
+    }
+  };
+  auto publish = [&](int stage) __attribute__((always_inline)) {
+    if (wave == 0) {
+      reinterpret_cast<float*>(smem + LREG)[stage * 64 + lane] = lse_next;
+      reinterpret_cast<float*>(smem + DREG)[stage * 64 + lane] = d_next;
+    }
+  };
+
+  // A operands.  Row fragments of S and dP: query 16 b + col, chunk 4 ks + g.
+  // Transposing reads of dV^T and dK^T: lane (g, col) points at query row
+  // 4 g + col / 4 (+ 16 for slots 4 .. 7), channels 16 nb + 4 (col % 4) .. + 3,
+  // and receives channel 16 nb + col of queries 4 g + e.
+  uint32_t qrow[KS], qtr[NB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qrow[ks] = TL::phys(col, 4 * ks + g);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) qtr[nb] = TL::phys(4 * g + (col >> 2), 2 * nb + ((col & 3) >> 1)) + 8 * (col & 1);
+  auto rowf = [&](uint32_t addr) __attribute__((always_inline)) {
+    return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4*>(smem + addr));
+  };
+  auto trf = [&](uint32_t addr) __attribute__((always_inline)) {
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x4 lo = lds_tr16(smem + addr);
+    const i16x4 hi = lds_tr16(smem + addr + 16 * TL::ROWB);
+    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(Frag, both);
+  };
+
+  f32x4 dkacc[NB], dvacc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dkacc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    dvacc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const float c = a.c;
+
+  // Step i: query tile i in stage st; tile i + 1 is fetched into st ^ 1.
+  auto step = [&](int i, int in, int st, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    wait_vmem();
+    publish(st);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS writes done (lgkmcnt(0))
+    __builtin_amdgcn_s_barrier();
+    if (in < nt) fetch(in, st ^ 1);
+    const int i0 = 64 * i;
+    const int qo = QREG + st * TL::BYTES, oo = OREG + st * TL::BYTES;
+    const float* lt = reinterpret_cast<const float*>(smem + LREG) + st * 64;
+    const float* dt = reinterpret_cast<const float*>(smem + DREG) + st * 64;
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      f32x4 s[2], dp[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        s[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        dp[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t ro = qrow[ks] + (32 * hq + 16 * b) * TL::ROWB;
+          s[b] = M::mma(rowf(ro + qo), kf[ks], s[b]);
+          dp[b] = M::mma(rowf(ro + oo), vf[ks], dp[b]);
+        }
+      // a 16-cycle product cannot hide an LDS read issued just before it
+      reads_ahead<4 * KS, 1, kNarrowRowAhead>();
+      // element-wise work at the higher issue priority: of the two waves on a
+      // SIMD, the one in its product phase needs a slot once per product
+      __builtin_amdgcn_s_setprio(1);
+      Frag pf, sf;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int rr = 32 * hq + 16 * b + 4 * g;  // queries i0 + rr .. + 3 against this lane's key
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[b][r], c, l4[r]));
+          if constexpr (!FULL) p = i0 + rr + r < sq.lq ? p : 0.0f;  // ragged last tile
+          pf[4 * b + r] = (T)p;
+          sf[4 * b + r] = (T)(p * (dp[b][r] - d4[r]));
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t to = qtr[nb] + 32 * hq * TL::ROWB;
+        dvacc[nb] = M::mma(trf(to + oo), pf, dvacc[nb]);
+        dkacc[nb] = M::mma(trf(to + qo), sf, dkacc[nb]);
+      }
+      reads_ahead<2 * NB, 2, kNarrowTrAhead>();
+    }
+  };
+
+  if (nt > 0) {
+    fetch(0, 0);
+    int i = 0;
+    for (; i < full1; ++i) step(i, i + 1, i & 1, std::true_type{});
+    for (; i < nt; ++i) step(i, i + 1, i & 1, std::false_type{});
+  }
+
+  if (mykey < Nk) {  // padding keys store zeros
+    T* dkrow = reinterpret_cast<T*>(a.dk) + headk + (size_t)mykey * D;
+    T* dvrow = reinterpret_cast<T*>(a.dv) + headk + (size_t)mykey * D;
+    const bool real = mykey < sq.lk;
+    const float sc = a.scale;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int d0 = 16 * nb + 4 * g;  // rows 4 g .. + 3 of channel block nb
+      float k4[4], v4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        k4[r] = real ? dkacc[nb][r] * sc : 0.0f;
+        v4[r] = real ? dvacc[nb][r] : 0.0f;
+      }
+      store4<T>(dkrow + d0, k4[0], k4[1], k4[2], k4[3]);
+      store4<T>(dvrow + d0, v4[0], v4[1], v4[2], v4[3]);
+    }
+  }
+}
+
 // Fill the kernel arguments shared by the dK/dV and dQ kernels; nblk is the
 // number of owned 128-row blocks per (batch, head).
 static Bwd16Args bwd16_args(const BwdProblem& p, int nblk) {
@@ -626,7 +853,12 @@ static_assert(kMaskBlock == 128, "a dK/dV workgroup's 128 keys are one mask bloc
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
   const Bwd16Args a = bwd16_args(p, (p.Nk + 127) / 128);
-  hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
+  // d = 128 without the causal mask: the 16-key kernel (1.45x on B=1 H=16
+  // N=8192); under the mask the 32-key kernel is 1-2% faster on long rows
+  if constexpr (D == 128 && !SPARSE && !DROP && !CAUSAL)
+    hipLaunchKernelGGL((dkdv16n_kernel<T>), dim3(a.total), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -71,6 +71,26 @@ template <> struct Mma<float> {
   }
 };
 
+// The 16x16x32 instruction for 16-bit operands (same rate per flop), checked
+// lane by lane on gfx950:
+//   A: lane l holds A[l%16][8*(l/16) + e], B: lane l holds B[8*(l/16) + e][l%16],
+//   C: lane l, register r holds C[4*(l/16) + r][l%16].
+template <typename T> struct Mma16;
+
+template <> struct Mma16<__bf16> {
+  using Frag = bf16x8;
+  __device__ static inline f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma16<_Float16> {
+  using Frag = f16x8;
+  __device__ static inline f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Fragment loads.
 

@@ -90,7 +90,11 @@ def test_bwd_sparse_matches_oracle(dtype, causal, shape, kind):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_all_ones_mask_is_the_dense_path(dtype):
-    """Every block kept: the same arithmetic as fa_fwd / fa_bwd, bit for bit."""
+    """Every block kept: the same arithmetic as fa_fwd / fa_bwd, bit for bit,
+    except dK/dV at d = 128 with 16-bit I/O, where the dense path runs its own
+    kernel (16 keys per wave) that adds the same products in another order:
+    there the two may differ by one rounding of the output type plus fp32
+    reordering noise."""
     dev = device()
     announce("sparse all-ones", dtype)
     q, k, v, do = to_dev(W.kv_inputs(2, 2, 700, 700, 128, dtype, 13001), dev)
@@ -102,8 +106,14 @@ def test_all_ones_mask_is_the_dense_path(dtype):
         g2 = fa.backward_sparse(q, k, v, o2, l2, do, ones, causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
-        for a, b in zip(g1, g2):
-            assert torch.equal(a, b)
+        assert torch.equal(g1[0], g2[0]), "dQ"
+        for a, b, what in zip(g1[1:], g2[1:], ("dK", "dV")):
+            if dtype == "f32":
+                assert torch.equal(a, b), what
+            else:
+                ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10   # one step of the output type, relative
+                af, bf = a.float(), b.float()
+                assert torch.all((af - bf).abs() <= ulp * bf.abs() + 1e-4 * bf.abs().max()), what
 
 
 def test_all_zero_mask():
