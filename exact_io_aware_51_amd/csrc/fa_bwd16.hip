@@ -602,13 +602,16 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
 }
 
 // --------------------------------------------------------------------------
-// dK, dV at d = 128 without dropout, a block mask or the causal mask (under
-// the causal mask the 32-key kernel measured 1-2% faster on long rows, and
-// runs there): a workgroup of eight
-// waves owns 128 keys, 16 per wave, so that two waves share each SIMD.  With
-// 32 keys per wave (dkdv16_kernel) the dK/dV accumulators and the stationary
-// K/V fragments alone take 192 registers and the kernel runs one wave per
-// SIMD; with 16 keys they take 96.  The products run on the 16x16x32
+// dK, dV at d = 128 without dropout or a block mask: each wave owns 16 keys,
+// so that two waves share each SIMD.  With 32 keys per wave (dkdv16_kernel)
+// the dK/dV accumulators and the stationary K/V fragments alone take 192
+// registers and that kernel runs one wave per SIMD; with 16 keys they take 96.
+// WAVES = 8 (no causal mask): one workgroup of 128 keys per CU.  WAVES = 4
+// (causal mask): two workgroups of 64 keys per CU, whose waves pair up on the
+// SIMDs out of step with each other, so one's element-wise work meets the
+// other's products; that measured 3-10% faster under the mask (the causal
+// grid's many short blocks) and 2.4% slower without it (each Q/dO tile is
+// streamed by twice as many workgroups).  The products run on the 16x16x32
 // instruction (the same rate per flop).  Per 32-query half and wave:
 // S = Q K^T and dP = dO V^T (two 16-query blocks, four 32-channel steps),
 // then dV^T += dO^T P and dK^T += Q^T dS (eight 16-channel blocks, the 32
@@ -618,8 +621,12 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
 // contraction slot 8 g + 4 b + r, and the transposing reads of dO and Q hand
 // the A operand the same queries in the same slots.  The Q and dO tiles keep
 // their 16-byte chunks permuted by Tile16n::sw, under which both read
-// patterns are conflict-free: 16 lanes reading one chunk of 16 consecutive
-// rows, and 32 lanes reading two adjacent chunks of 8 consecutive rows.
+// patterns are conflict-free on gfx950, where a 16-byte read is served in
+// four passes of the 16 lanes that agree in lane bits 2 and 4, and an 8-byte
+// read in two passes of 32 consecutive lanes (inferred from bank-conflict
+// counts of isolated read patterns): the row fragments (one chunk of 16
+// consecutive rows per 16 lanes) and the transposing reads (two adjacent
+// chunks of 8 consecutive rows per 32 lanes).
 // Operand reads kept in flight ahead of the 16x16x32 products: row fragments
 // of S / dP, and transposing pairs of dV / dK.
 constexpr int kNarrowRowAhead = 8;
@@ -628,17 +635,18 @@ constexpr int kNarrowTrAhead = 4;
 struct Tile16n {
   static constexpr int ROWB = 256;    // one row of 128 16-bit values
   static constexpr int BYTES = 64 * ROWB;
-  static constexpr int ROUNDS = 2;    // direct loads per tile and wave (eight waves)
-  __device__ static constexpr int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+  __device__ static constexpr int sw(int r) { return (r ^ (r << 1)) & 15; }
   __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
 };
 
-template <typename T>
-__global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
+template <typename T, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Args a) {
   using M = Mma16<T>;
   using Frag = typename M::Frag;
   using TL = Tile16n;
   constexpr int D = 128;
+  constexpr int KEYS = 16 * WAVES;       // keys per workgroup
+  constexpr int ROUNDS = TL::BYTES / (1024 * WAVES);  // direct loads per tile and wave
   constexpr int KS = D / 32;             // contraction steps of S and dP
   constexpr int NB = D / 16;             // 16-channel blocks of dK^T and dV^T
   constexpr int QREG = 0;                // [Q0 Q1 dO0 dO1 lse0 lse1 D0 D1]
@@ -654,9 +662,9 @@ __global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
   const int g = lane >> 4, col = lane & 15;
   const int Nq = a.Nq, Nk = a.Nk;
 
-  int bh, kblk;
-  block_order<32>(block_id(), a.total, a.nblk, false, &bh, &kblk);
-  const int kb0 = kblk * 128;
+  int bh, kblk;  // under the causal mask key block 0 is seen by the most query tiles
+  block_order<32 * (8 / WAVES)>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
+  const int kb0 = kblk * KEYS;
   const int kw = kb0 + 16 * wave;
   const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
   const size_t headq = (size_t)bh * (size_t)Nq * D, headk = (size_t)bh * (size_t)Nk * D;
@@ -678,17 +686,25 @@ __global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
     }
   }
 
-  // query tiles of real queries (a block of padding keys visits none); the
-  // last one is ragged unless lq is a multiple of 64
+  // query tiles of real queries (a block of padding keys visits none), as in
+  // dkdv16_kernel: under the causal mask key kb0 is first seen by query
+  // kb0 - off, and every query from kb0 + KEYS - 1 - off on sees all keys
   const int nt = kb0 < sq.lk ? (sq.lq + 63) / 64 : 0;
+  int first = 0, full0 = 0;
+  if (CAUSAL) {
+    const int f = floor_div(kb0 - sq.off, 64);
+    first = f > 0 ? f : 0;
+    const int gq = floor_div(kb0 + KEYS - 1 - sq.off + 63, 64);
+    full0 = gq > first ? gq : first;
+  }
   const int full1 = sq.lq / 64;
 
-  // direct loads: slot s = (8 r + wave) * 64 + lane, 16 bytes at LDS byte 16 s,
-  // holds logical chunk (s % 16) ^ sw(row) of row s / 16
-  uint32_t goff[TL::ROUNDS];
+  // direct loads: slot s = (WAVES r + wave) * 64 + lane, 16 bytes at LDS byte
+  // 16 s, holds logical chunk (s % 16) ^ sw(row) of row s / 16
+  uint32_t goff[ROUNDS];
 #pragma unroll
-  for (int r = 0; r < TL::ROUNDS; ++r) {
-    const int sl = (r * 8 + wave) * 64 + lane;
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int sl = (r * WAVES + wave) * 64 + lane;
     const int row = sl >> 4, pc = sl & 15;
     goff[r] = row * TL::ROWB + ((pc ^ TL::sw(row)) << 4);
   }
@@ -698,9 +714,9 @@ __global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
     const auto rq = buffer_rsrc(Qg + (size_t)row0 * TL::ROWB, tile_bytes(sq.lq - row0, 64, TL::ROWB));
     const auto ro = buffer_rsrc(Og + (size_t)row0 * TL::ROWB, tile_bytes(sq.lq - row0, 64, TL::ROWB));
 #pragma unroll
-    for (int r = 0; r < TL::ROUNDS; ++r) {
-      lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * 8 + wave) * 1024, goff[r]);
-      lds_load16(ro, smem + OREG + stage * TL::BYTES + (r * 8 + wave) * 1024, goff[r]);
+    for (int r = 0; r < ROUNDS; ++r) {
+      lds_load16(rq, smem + QREG + stage * TL::BYTES + (r * WAVES + wave) * 1024, goff[r]);
+      lds_load16(ro, smem + OREG + stage * TL::BYTES + (r * WAVES + wave) * 1024, goff[r]);
     }
     if (wave == 0) {
       const int qi = row0 + lane;
@@ -752,6 +768,7 @@ __global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
     __builtin_amdgcn_s_barrier();
     if (in < nt) fetch(in, st ^ 1);
     const int i0 = 64 * i;
+    if (!FULL && CAUSAL && i0 + 63 + sq.off < kw) return;  // no query of the tile sees this wave's keys
     const int qo = QREG + st * TL::BYTES, oo = OREG + st * TL::BYTES;
     const float* lt = reinterpret_cast<const float*>(smem + LREG) + st * 64;
     const float* dt = reinterpret_cast<const float*>(smem + DREG) + st * 64;
@@ -785,7 +802,10 @@ __global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[b][r], c, l4[r]));
-          if constexpr (!FULL) p = i0 + rr + r < sq.lq ? p : 0.0f;  // ragged last tile
+          if constexpr (!FULL) {
+            const int qi = i0 + rr + r;
+            p = (qi < sq.lq && (!CAUSAL || mykey <= qi + sq.off)) ? p : 0.0f;
+          }
           pf[4 * b + r] = (T)p;
           sf[4 * b + r] = (T)(p * (dp[b][r] - d4[r]));
         }
@@ -801,11 +821,12 @@ __global__ __launch_bounds__(512, 1) void dkdv16n_kernel(Bwd16Args a) {
     }
   };
 
-  if (nt > 0) {
-    fetch(0, 0);
-    int i = 0;
-    for (; i < full1; ++i) step(i, i + 1, i & 1, std::true_type{});
-    for (; i < nt; ++i) step(i, i + 1, i & 1, std::false_type{});
+  if (first < nt) {
+    fetch(first, 0);
+    int i = first;
+    for (; i < nt && i < full0; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
+    for (; i < full1; ++i) step(i, i + 1, (i - first) & 1, std::true_type{});
+    for (; i < nt; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
   }
 
   if (mykey < Nk) {  // padding keys store zeros
@@ -852,13 +873,14 @@ static_assert(kMaskBlock == 128, "a dK/dV workgroup's 128 keys are one mask bloc
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
-  const Bwd16Args a = bwd16_args(p, (p.Nk + 127) / 128);
-  // d = 128 without the causal mask: the 16-key kernel (1.45x on B=1 H=16
-  // N=8192); under the mask the 32-key kernel is 1-2% faster on long rows
-  if constexpr (D == 128 && !SPARSE && !DROP && !CAUSAL)
-    hipLaunchKernelGGL((dkdv16n_kernel<T>), dim3(a.total), dim3(512), 0, stream, a);
-  else
+  if constexpr (D == 128 && !SPARSE && !DROP) {  // 16 keys per wave
+    constexpr int WAVES = CAUSAL ? 4 : 8;
+    const Bwd16Args a = bwd16_args(p, (p.Nk + 16 * WAVES - 1) / (16 * WAVES));
+    hipLaunchKernelGGL((dkdv16n_kernel<T, CAUSAL, WAVES>), dim3(a.total), dim3(64 * WAVES), 0, stream, a);
+  } else {
+    const Bwd16Args a = bwd16_args(p, (p.Nk + 127) / 128);
     hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
