@@ -602,7 +602,7 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
 }
 
 // --------------------------------------------------------------------------
-// dK, dV at d = 128 without dropout or a block mask: each wave owns 16 keys,
+// dK, dV at d = 128 (dense, block-sparse, dropout): each wave owns 16 keys,
 // so that two waves share each SIMD.  With 32 keys per wave (dkdv16_kernel)
 // the dK/dV accumulators and the stationary K/V fragments alone take 192
 // registers and that kernel runs one wave per SIMD; with 16 keys they take 96.
@@ -639,7 +639,7 @@ struct Tile16n {
   __device__ static constexpr int phys(int r, int chunk) { return r * ROWB + ((chunk ^ sw(r)) << 4); }
 };
 
-template <typename T, bool CAUSAL, int WAVES>
+template <typename T, bool CAUSAL, bool SPARSE, bool DROP, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Args a) {
   using M = Mma16<T>;
   using Frag = typename M::Frag;
@@ -698,6 +698,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Arg
     full0 = gq > first ? gq : first;
   }
   const int full1 = sq.lq / 64;
+  // block-sparse: the 128-key mask column of this workgroup's keys, packed
+  // into bits in LDS; a query tile is live unless its 128-row block is masked out
+  __shared__ uint64_t mwords[SPARSE ? kMaxMaskWords : 1];
+  if constexpr (SPARSE) {
+    pack_mask_words(mwords, a.block_mask + (size_t)bh * a.nbq * a.nbk + (kb0 >> 7), a.nbq, a.nbk, lane, wave, WAVES);
+    __syncthreads();
+  }
 
   // direct loads: slot s = (WAVES r + wave) * 64 + lane, 16 bytes at LDS byte
   // 16 s, holds logical chunk (s % 16) ^ sw(row) of row s / 16
@@ -799,6 +806,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Arg
         const int rr = 32 * hq + 16 * b + 4 * g;  // queries i0 + rr .. + 3 against this lane's key
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lt + rr);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dt + rr);
+        // dropout keep bits of queries i0 + rr .. + 3 against this lane's key: a
+        // DPP quad holds four consecutive keys against the same four queries
+        const uint32_t kbits = DROP ? a.drop.quad_keep(mykey >> 2, i0 + rr, bh, col & 3) : 0u;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[b][r], c, l4[r]));
@@ -806,8 +816,16 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Arg
             const int qi = i0 + rr + r;
             p = (qi < sq.lq && (!CAUSAL || mykey <= qi + sq.off)) ? p : 0.0f;
           }
-          pf[4 * b + r] = (T)p;
-          sf[4 * b + r] = (T)(p * (dp[b][r] - d4[r]));
+          if constexpr (DROP) {
+            // dV takes the kept weights (1 / (1 - p) applied at the store); dP of
+            // a dropped weight is 0, of a kept one dP / (1 - p)
+            const bool kp = (kbits >> (4 * r)) & 1u;
+            pf[4 * b + r] = (T)(kp ? p : 0.0f);
+            sf[4 * b + r] = (T)(p * ((kp ? dp[b][r] * a.drop.scale : 0.0f) - d4[r]));
+          } else {
+            pf[4 * b + r] = (T)p;
+            sf[4 * b + r] = (T)(p * (dp[b][r] - d4[r]));
+          }
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -821,12 +839,38 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Arg
     }
   };
 
-  if (first < nt) {
-    fetch(first, 0);
-    int i = first;
-    for (; i < nt && i < full0; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
-    for (; i < full1; ++i) step(i, i + 1, (i - first) & 1, std::true_type{});
-    for (; i < nt; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
+  if constexpr (!SPARSE) {
+    if (first < nt) {
+      fetch(first, 0);
+      int i = first;
+      for (; i < nt && i < full0; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
+      for (; i < full1; ++i) step(i, i + 1, (i - first) & 1, std::true_type{});
+      for (; i < nt; ++i) step(i, i + 1, (i - first) & 1, std::false_type{});
+    }
+  } else {
+    // only live query tiles, in increasing order, alternating stages; masked
+    // and unmasked tiles in loops of their own, as in dkdv16_kernel
+    auto next = [&](int i) __attribute__((always_inline)) { return next_live_tile(mwords, i, 2, a.nbq, nt); };
+    int i = live_tile_from(mwords, first, 2, a.nbq, nt);
+    if (i < nt) {
+      fetch(i, 0);
+      int st = 0;
+      for (; i < nt && i < full0; st ^= 1) {
+        const int in = next(i);
+        step(i, in, st, std::false_type{});
+        i = in;
+      }
+      for (; i < full1; st ^= 1) {
+        const int in = next(i);
+        step(i, in, st, std::true_type{});
+        i = in;
+      }
+      for (; i < nt; st ^= 1) {
+        const int in = next(i);
+        step(i, in, st, std::false_type{});
+        i = in;
+      }
+    }
   }
 
   if (mykey < Nk) {  // padding keys store zeros
@@ -834,6 +878,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Arg
     T* dvrow = reinterpret_cast<T*>(a.dv) + headk + (size_t)mykey * D;
     const bool real = mykey < sq.lk;
     const float sc = a.scale;
+    const float sv = DROP ? a.drop.scale : 1.0f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int d0 = 16 * nb + 4 * g;  // rows 4 g .. + 3 of channel block nb
@@ -841,7 +886,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void dkdv16n_kernel(Bwd16Arg
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         k4[r] = real ? dkacc[nb][r] * sc : 0.0f;
-        v4[r] = real ? dvacc[nb][r] : 0.0f;
+        v4[r] = real ? dvacc[nb][r] * sv : 0.0f;
       }
       store4<T>(dkrow + d0, k4[0], k4[1], k4[2], k4[3]);
       store4<T>(dvrow + d0, v4[0], v4[1], v4[2], v4[3]);
@@ -873,10 +918,10 @@ static_assert(kMaskBlock == 128, "a dK/dV workgroup's 128 keys are one mask bloc
 
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
 static hipError_t launch_dkdv16_t(const BwdProblem& p, hipStream_t stream) {
-  if constexpr (D == 128 && !SPARSE && !DROP) {  // 16 keys per wave
+  if constexpr (D == 128) {  // 16 keys per wave
     constexpr int WAVES = CAUSAL ? 4 : 8;
     const Bwd16Args a = bwd16_args(p, (p.Nk + 16 * WAVES - 1) / (16 * WAVES));
-    hipLaunchKernelGGL((dkdv16n_kernel<T, CAUSAL, WAVES>), dim3(a.total), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((dkdv16n_kernel<T, CAUSAL, SPARSE, DROP, WAVES>), dim3(a.total), dim3(64 * WAVES), 0, stream, a);
   } else {
     const Bwd16Args a = bwd16_args(p, (p.Nk + 127) / 128);
     hipLaunchKernelGGL((dkdv16_kernel<T, D, CAUSAL, SPARSE, DROP>), dim3(a.total), dim3(256), 0, stream, a);
