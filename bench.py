@@ -613,6 +613,57 @@ def time_fwd_fp8(name, dev, iters=20, warmup=3, fmt="e4m3"):
             "shape": f"{fmt} in, bf16 out, B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
+def time_variants(dev, iters=10, warmup=2):
+    """Block-sparse and dropout entry points against the dense ones on the same inputs
+    (bf16): forward and whole backward, time per call and the ratio to dense."""
+    import torch
+
+    import exact_io_aware_51_amd as fa
+    from exact_io_aware_51_amd import workloads as W
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    out = {"sparse": {}, "dropout": {}}
+    for B, H, N, d in ((1, 8, 32768, 128), (2, 16, 4096, 128)):
+        q, k, v, do = (t.to(dev) for t in W.kv_inputs(B, H, N, N, d, "bf16", 4242))
+        o, lse = fa.forward(q, k, v, causal=True)
+        fd = timed(lambda: fa.forward(q, k, v, causal=True))
+        bd = timed(lambda: fa.backward(q, k, v, o, lse, do, causal=True))
+        for keep in (1.0, 0.5, 0.25):
+            m = W.block_mask(B, H, N, keep, 77).to(dev)
+            if keep == 1.0:
+                m.fill_(1)
+            os_, ls_ = fa.forward_sparse(q, k, v, m, causal=True)
+            fs = timed(lambda: fa.forward_sparse(q, k, v, m, causal=True))
+            bs = timed(lambda: fa.backward_sparse(q, k, v, os_, ls_, do, m, causal=True))
+            out["sparse"][f"B={B} H={H} N={N} d={d} causal, {int(keep * 100)}% kept"] = {
+                "fwd_ms": round(fs, 4), "fwd_vs_dense": round(fs / fd, 3),
+                "bwd_ms": round(bs, 4), "bwd_vs_dense": round(bs / bd, 3)}
+    for B, H, N, d, causal in ((1, 16, 16384, 128, False), (1, 16, 16384, 128, True), (2, 16, 4096, 128, True),
+                               (4, 16, 4096, 64, True)):
+        q, k, v, do = (t.to(dev) for t in W.kv_inputs(B, H, N, N, d, "bf16", 4343))
+        o, lse = fa.forward(q, k, v, causal=causal)
+        fd = timed(lambda: fa.forward(q, k, v, causal=causal))
+        bd = timed(lambda: fa.backward(q, k, v, o, lse, do, causal=causal))
+        od, ld = fa.forward_dropout(q, k, v, 0.1, 1234, causal=causal)
+        fr = timed(lambda: fa.forward_dropout(q, k, v, 0.1, 1234, causal=causal))
+        br = timed(lambda: fa.backward_dropout(q, k, v, od, ld, do, 0.1, 1234, causal=causal))
+        out["dropout"][f"B={B} H={H} N={N} d={d} {'causal' if causal else 'non-causal'}, p=0.1"] = {
+            "fwd_ms": round(fr, 4), "fwd_vs_dense": round(fr / fd, 3),
+            "bwd_ms": round(br, 4), "bwd_vs_dense": round(br / bd, 3)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -622,6 +673,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-fwd-workloads", action="store_true", help="skip the forward-only lines for c1..c4")
+    ap.add_argument("--variants", action="store_true",
+                    help="diagnostic: block-sparse and dropout entry points against dense, one JSON line")
     ap.add_argument("--fwd-workload", default=None,
                     help="diagnostic: time only the forward kernel of this workload (c1..c5), one JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -670,6 +723,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
+        return
+    if args.variants:
+        print(json.dumps(time_variants(dev)), flush=True)
         return
     if args.fwd_workload:
         res = time_fwd_only(args.fwd_workload, dev, iters=args.steps, warmup=args.warmup)
