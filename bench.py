@@ -513,64 +513,128 @@ def time_fwd_only(name, dev, iters=20, warmup=3):
             "shape": f"{w.dtype} B={w.B} H={w.H} N={w.N} d={w.d} {'causal' if w.causal else 'non-causal'}"}
 
 
-def _gfx_clocks_mhz():
-    """Current GFX clock of every XCD from amd-smi (MHz), or [] if it cannot be read."""
+def _amd_smi(args):
+    """Parsed JSON of `amd-smi <args> --json`, or None if the tool or its output is unavailable."""
     import subprocess
     try:
-        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=15)
-        data = json.loads(r.stdout)
+        r = subprocess.run(["amd-smi", *args, "--json"], capture_output=True, text=True, timeout=15)
+        return json.loads(r.stdout)
     except Exception:  # noqa: BLE001 - best effort: a missing tool only drops the field
-        return []
+        return None
+
+
+def _walk(x, visit):
+    if isinstance(x, dict):
+        for key, val in x.items():
+            if not visit(key, val):
+                _walk(val, visit)
+    elif isinstance(x, list):
+        for val in x:
+            _walk(val, visit)
+
+
+def _gfx_clocks_mhz():
+    """Current GFX clock of every XCD from amd-smi (MHz), or [] if it cannot be read."""
     out = []
 
-    def walk(x):
-        if isinstance(x, dict):
-            for key, val in x.items():
-                if key.startswith("gfx_") and isinstance(val, dict) and isinstance(val.get("clk"), dict):
-                    v = val["clk"].get("value")
-                    if isinstance(v, (int, float)):
-                        out.append(float(v))
-                else:
-                    walk(val)
-        elif isinstance(x, list):
-            for val in x:
-                walk(val)
-    walk(data)
+    def visit(key, val):
+        if key.startswith("gfx_") and isinstance(val, dict) and isinstance(val.get("clk"), dict):
+            v = val["clk"].get("value")
+            if isinstance(v, (int, float)):
+                out.append(float(v))
+            return True
+        return False
+    _walk(_amd_smi(["metric", "--clock"]), visit)
     return out
 
 
-def clock_under_load(name, dev, seconds=3.0):
-    """Mean GFX clock (MHz) sampled with amd-smi while workload `name`'s forward runs back to back."""
+def _socket_power_w():
+    """Current socket power of the GPU from amd-smi (W), or None if it cannot be read."""
+    out = []
+
+    def visit(key, val):
+        if key == "socket_power" and isinstance(val, dict) and isinstance(val.get("value"), (int, float)):
+            out.append(float(val["value"]))
+            return True
+        return False
+    _walk(_amd_smi(["metric", "--power"]), visit)
+    return out[0] if out else None
+
+
+def sample_under_load(run, seconds=3.0):
+    """Mean GFX clock (MHz) and median socket power (W), sampled with amd-smi while run() is called
+    back to back for about `seconds`; None if amd-smi gives no clock."""
     import threading
 
     import torch
-
-    from exact_io_aware_51_amd import workloads as W
-    w = W.WORKLOADS[name]
-    r = Runner(w, dev)
-    samples, stop = [], threading.Event()
+    clocks, powers, stop = [], [], threading.Event()
 
     def sampler():
         while not stop.is_set():
             c = _gfx_clocks_mhz()
             if not c:
                 return
-            samples.append(sum(c) / len(c))
-    r.fwd()
+            clocks.append(sum(c) / len(c))
+            pw = _socket_power_w()
+            if pw is not None:
+                powers.append(pw)
+    run()
     torch.cuda.synchronize()
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        r.fwd()
+        run()
         torch.cuda.synchronize()
     stop.set()
-    th.join(timeout=20)
-    if len(samples) < 2:
+    th.join(timeout=30)
+    if len(clocks) < 2:
         return None
-    busy = samples[1:]  # the first sample may predate the load
-    return {"workload": f"{name} forward", "gfx_mhz_mean": round(sum(busy) / len(busy), 1), "samples": len(busy),
-            "source": "amd-smi metric --clock (mean over XCDs)"}
+    busy = clocks[1:]  # the first sample may predate the load
+    pw = sorted(powers[1:])
+    return {"gfx_mhz_mean": round(sum(busy) / len(busy), 1), "socket_power_w": pw[len(pw) // 2] if pw else None,
+            "samples": len(busy), "source": "amd-smi metric --clock / --power"}
+
+
+def clock_under_load(name, dev, seconds=3.0):
+    """GFX clock and socket power while workload `name`'s forward runs back to back."""
+    from exact_io_aware_51_amd import workloads as W
+    r = Runner(W.WORKLOADS[name], dev)
+    got = sample_under_load(r.fwd, seconds)
+    if got is None:
+        return None
+    return {"workload": f"{name} forward", **got}
+
+
+def matmul_ceiling(dev, n=8192, iters=10, seconds=3.0):
+    """Context, not part of the path: the dense bf16 matrix rate a vendor GEMM (torch.matmul, which
+    calls hipBLASLt) reaches on this GPU, n x n x n, with the clock and power it runs at.  It shows
+    what the matrix cores deliver under the board's power limit, next to the 2.5 PFLOP/s peak that
+    assumes the 2.4 GHz clock."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+
+    def run():
+        for _ in range(iters):
+            torch.matmul(a, b, out=c)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    out = {"what": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), context only", "ms": round(ms, 4),
+           "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    load = sample_under_load(run, seconds)
+    if load is not None:
+        out.update({k: load[k] for k in ("gfx_mhz_mean", "socket_power_w")})
+    return out
 
 
 def time_fwd_fp8(name, dev, iters=20, warmup=3, fmt="e4m3"):
@@ -823,6 +887,8 @@ def main():
             clk["c4_frac_of_peak_at_this_clock"] = round(
                 fw["c4"]["tflops"] / (PEAK_TFLOPS["bf16"] * clk["gfx_mhz_mean"] / 2400.0), 4)
         out["clock"] = clk
+        log("bench: vendor GEMM rate on this GPU (context)")
+        out["matmul_ceiling"] = matmul_ceiling(dev)
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

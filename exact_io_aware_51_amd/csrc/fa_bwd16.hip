@@ -350,19 +350,18 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
 }
 
 // --------------------------------------------------------------------------
-// dK, dV: a workgroup owns 128 keys (32 per wave; K and V rows in VGPRs as
-// the stationary B operands) and streams 64-query tiles of Q and dO, with the
-// query rows' LSE (pre-scaled to log2 units) and D, through LDS.  Per
-// 32-query half: S = Q K^T and dP = dO V^T, then P and dS element-wise, then
-// dV^T += dO^T P and dK^T += Q^T dS with the transposing reads of dO and Q.
-// The four accumulators (dK^T, dV^T) and the stationary fragments need about
-// 280 VGPRs, so one wave per SIMD runs this kernel; the element-wise work of
-// one half overlaps the matrix ops of the other inside the wave.
-// d = 64 (no dropout): the kernel fits 256 VGPRs without spills, so two waves
-// share each SIMD; measured 1.5x faster than one.  d = 128 needs ~450 and the
-// dropout instantiations spill at 256: one wave.
+// dK, dV at d = 64 (d = 128 runs dkdv16n_kernel below): a workgroup owns 128
+// keys (32 per wave; K and V rows in VGPRs as the stationary B operands) and
+// streams 64-query tiles of Q and dO, with the query rows' LSE (pre-scaled to
+// log2 units) and D, through LDS.  Per 32-query half: S = Q K^T and
+// dP = dO V^T, then P and dS element-wise, then dV^T += dO^T P and
+// dK^T += Q^T dS with the transposing reads of dO and Q.  Without dropout the
+// kernel fits 256 VGPRs with no spills, so two waves share each SIMD
+// (measured 1.5x faster than one); the dropout instantiations would spill at
+// 256 and run one wave per SIMD.
 template <typename T, int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel(Bwd16Args a) {
+__global__ __launch_bounds__(256, DROP ? 1 : 2) void dkdv16_kernel(Bwd16Args a) {
+  static_assert(D == 64, "d = 128 has its own kernel");
   using M = Mma<T>;
   using TL = Tile16<D>;
   using Frag = typename M::Frag;
@@ -382,7 +381,7 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
   const int Nq = a.Nq, Nk = a.Nk;
 
   int bh, kblk;  // under the causal mask key block 0 is seen by the most query tiles
-  block_order<((D == 64 && !DROP) ? 64 : 32)>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
+  block_order<(DROP ? 32 : 64)>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
   const int kb0 = kblk * 128;
   const int kw = kb0 + 32 * wave;
   const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
@@ -603,9 +602,10 @@ __global__ __launch_bounds__(256, (D == 64 && !DROP) ? 2 : 1) void dkdv16_kernel
 
 // --------------------------------------------------------------------------
 // dK, dV at d = 128 (dense, block-sparse, dropout): each wave owns 16 keys,
-// so that two waves share each SIMD.  With 32 keys per wave (dkdv16_kernel)
-// the dK/dV accumulators and the stationary K/V fragments alone take 192
-// registers and that kernel runs one wave per SIMD; with 16 keys they take 96.
+// so that two waves share each SIMD.  With 32 keys per wave (the layout of
+// dkdv16_kernel) the d = 128 dK/dV accumulators and stationary K/V fragments
+// alone would take 192 registers, leaving one wave per SIMD; with 16 keys
+// they take 96.
 // WAVES = 8 (no causal mask): one workgroup of 128 keys per CU.  WAVES = 4
 // (causal mask): two workgroups of 64 keys per CU, whose waves pair up on the
 // SIMDs out of step with each other, so one's element-wise work meets the

@@ -81,3 +81,17 @@ def test_trace_summary_takes_the_step_kernels(bench, tmp_path):
     assert float(rows["fa_bwd_dkdv"][3]) == pytest.approx(301 + 1.0, abs=0.05)   # mean of 301, 302, 303
     assert float(rows["fa_fwd"][3]) == pytest.approx(100.0, abs=0.05)
     assert "Step (sum of the kernels' averages): 602.0 us" in text
+
+
+def test_amd_smi_parsing(bench, monkeypatch):
+    """Clock and power readers take the fields amd-smi's JSON gives per GPU and XCD."""
+    clock = {"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}},
+                                               "gfx_1": {"clk": {"value": 1900, "unit": "MHz"}},
+                                               "mem_0": {"clk": {"value": 1300, "unit": "MHz"}}}}]}
+    power = {"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": 1350, "unit": "W"},
+                                               "gfx_voltage": "N/A"}}]}
+    monkeypatch.setattr(bench, "_amd_smi", lambda args: clock if "--clock" in args else power)
+    assert bench._gfx_clocks_mhz() == [2100.0, 1900.0]
+    assert bench._socket_power_w() == 1350.0
+    monkeypatch.setattr(bench, "_amd_smi", lambda args: None)
+    assert bench._gfx_clocks_mhz() == [] and bench._socket_power_w() is None
