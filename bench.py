@@ -86,7 +86,7 @@ def traffic_for(kernel):
     return entry.get("hbm_bytes_per_launch")
 
 
-STEP_KERNELS = {"fwd16_kernel": "fwd", "dkdv16": "bwd_dkdv", "dq16_kernel": "bwd_dq"}  # dkdv16_kernel, dkdv16n_kernel
+STEP_KERNELS = {"fwd16_kernel": "fwd", "dkdv": "bwd_dkdv", "dq16_kernel": "bwd_dq"}  # dkdv16_kernel, dkdv16n_kernel, dkdv32s_kernel
 
 
 # --------------------------------------------------------------- counter reports

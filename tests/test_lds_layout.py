@@ -20,6 +20,14 @@ address), hand the 16x16x32 product the A operand matching P taken from the
 accumulators (query of contraction slot (g, e): 16 (e / 4) + 4 g + e % 4), so
 that the products are exactly dO^T P and Q K^T, and that the direct loads of
 four- and eight-wave workgroups place every chunk where the reads expect it.
+
+The kernel with K and V resident in LDS (dkdv32s_kernel) keeps 128 K and 128 V
+rows in the same layout and reads them as row fragments (lane l: key row
+32 kg + 16 u + l % 16, chunk 4 ks + l / 16) for the B operand of S and dP; its
+Q / dO row fragments and transposing reads are those above with the wave's
+query half (32 qh rows) as offset.  The tests check those key reads, the
+products S = Q K^T they give, the direct loads of 128-row tiles by eight waves
+and the layout of the partial sums two waves combine at the end.
 """
 import numpy as np
 
@@ -104,7 +112,7 @@ def test_transposing_reads_are_conflict_free_and_in_bounds():
 
 
 def _tile(values):
-    mem = np.zeros(ROWS * ROWB // 2)
+    mem = np.zeros(values.shape[0] * ROWB // 2)
     for q in range(values.shape[0]):
         for c in range(values.shape[1]):
             byte = phys(q, (2 * c) // 16) + (2 * c) % 16
@@ -179,3 +187,65 @@ def test_direct_loads_place_every_chunk():
         for row in range(ROWS):
             for c in range(CPR):
                 assert placed[phys(row, c)] == row * ROWB + 16 * c
+
+
+def key_row_addr(l, kg, u, ks):
+    return phys(32 * kg + 16 * u + (l & 15), 4 * ks + (l >> 4))
+
+
+def test_resident_key_rows_are_conflict_free_and_in_bounds():
+    for kg in range(4):
+        for u in range(2):
+            for ks in range(4):
+                a = [key_row_addr(l, kg, u, ks) for l in range(64)]
+                assert all(0 <= x and x + 16 <= 2 * ROWS * ROWB for x in a)
+                assert _worst_conflict(a, 16) == 1, (kg, u, ks)
+
+
+def test_resident_keys_give_Q_K_transpose():
+    """S of query block (qh, b) against key block (kg, kb): Q row fragments as A, K row fragments as B."""
+    rng = np.random.default_rng(3)
+    Q = rng.integers(-3, 4, (64, 128)).astype(np.float64)
+    K = rng.integers(-3, 4, (128, 128)).astype(np.float64)
+    mq, mk = _tile(Q), _tile(K)
+    for qh in range(2):
+        for kg in range(4):
+            for b in range(2):
+                for kb in range(2):
+                    S = np.zeros((16, 16))
+                    for ks in range(4):
+                        A = np.array([mq[row_addr(l, 2 * qh + b, ks) // 2: row_addr(l, 2 * qh + b, ks) // 2 + 8]
+                                      for l in range(64)])
+                        Bk = np.array([mk[key_row_addr(l, kg, kb, ks) // 2: key_row_addr(l, kg, kb, ks) // 2 + 8]
+                                       for l in range(64)])
+                        S += _product(A, Bk)
+                    q0, k0 = 32 * qh + 16 * b, 32 * kg + 16 * kb
+                    assert np.array_equal(S, Q[q0:q0 + 16] @ K[k0:k0 + 16].T), (qh, kg, b, kb)
+
+
+def test_direct_loads_place_128_key_rows():
+    """Eight waves x 64 lanes x 4 rounds fill a 128-row tile: slot s at LDS byte 16 s holds
+    logical chunk (s % 16) ^ sw(row) of row s / 16."""
+    placed = {}
+    for r in range(4):
+        for w in range(8):
+            for l in range(64):
+                s = (r * 8 + w) * 64 + l
+                row, pc = s // CPR, s % CPR
+                assert 16 * s + 16 <= 2 * ROWS * ROWB
+                placed[16 * s] = row * ROWB + ((pc ^ sw(row)) << 4)
+    assert len(placed) == 2 * ROWS * CPR
+    for row in range(2 * ROWS):
+        for c in range(CPR):
+            assert placed[phys(row, c)] == row * ROWB + 16 * c
+
+
+def test_partial_sum_layout():
+    """The second wave of each key group writes (kg, nb, kb, r, lane) once each; dK and dV
+    partials together fit the 128 KiB of tiles they overwrite."""
+    NB = 8
+    red = 4 * NB * 2 * 4 * 64
+    offs = {(((kg * NB + nb) * 2 + kb) * 4 + r) * 64 + lane
+            for kg in range(4) for nb in range(NB) for kb in range(2) for r in range(4) for lane in range(64)}
+    assert offs == set(range(red))
+    assert 2 * red * 4 <= 8 * ROWS * ROWB
