@@ -4,7 +4,7 @@ This module only draws random numbers and names shapes; it holds none of the
 attention arithmetic, so the CPU oracle and the HIP path can both take their
 inputs from it without sharing any computation.
 
-The five workloads are the ones the method is judged on (the page "How Flash
+The five workloads are the shapes the attention path is measured on (the page "How Flash
 Attention Works: Tiling, Softmax, GPU I/O" motivates the long-context sizes in
 its introduction and in "Why Standard Attention Becomes a GPU Memory I/O
 Bottleneck"; the page "attn-flash-equivalence" quotes n = 8192, fp16 in
