@@ -2,8 +2,9 @@
 """Throughput of the fused exact-attention hot path on one MI355X.
 
 One step = the whole path on one batch of synthetic input: the forward kernel
-(O, LSE) followed by the three backward stages (row sums D, dK/dV, dQ) of the
-fwd+bwd workload c5 (bf16, B=2, H=16, N=4096, d=128, causal).  Inputs are
+(O, LSE) followed by the two backward stages (dQ, which also forms the row sums
+D, then dK/dV) of the fwd+bwd workload c5 (bf16, B=2, H=16, N=4096, d=128,
+causal).  Inputs are
 resident in device memory before the timed region starts.  Each kernel is
 bracketed by HIP events on the stream it is launched on, so the per-kernel
 averages (and the roofline of the dominant kernel) are measured live.
@@ -11,6 +12,11 @@ averages (and the roofline of the dominant kernel) are measured live.
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Other modes (each prints its own JSON): --variants (block-sparse and dropout
+against dense), --sweep (rates across shapes), --fwd-workload NAME (one forward
+workload), --copy-calibration MIB, and the report writers --counters-from,
+--trace-summary-from.
 """
 from __future__ import annotations
 
@@ -728,6 +734,52 @@ def time_variants(dev, iters=10, warmup=2):
     return out
 
 
+SWEEP_SHAPES = ((8, 16, 1024), (4, 16, 2048), (2, 16, 4096), (1, 16, 8192), (1, 16, 16384), (1, 8, 32768))
+
+
+def time_sweep(dev, rounds=5):
+    """Forward, dQ (with the row sums) and dK/dV across sequence lengths, head sizes and masks
+    (bf16, seeded N(0,1) inputs): best of `rounds` timed loops per kernel, TFLOP/s with causal
+    flops halved; the backward's rate is its algorithmic 10 N_eff d over the two kernels' times."""
+    import torch
+
+    from exact_io_aware_51_amd import workloads as W
+
+    def best(fn, iters):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t = float("inf")
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(iters):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t = min(t, e0.elapsed_time(e1) / iters)
+        return t
+
+    rows = []
+    for B, H, N in SWEEP_SHAPES:
+        for d in (64, 128):
+            for causal in (True, False):
+                w = W.shape_case(B, H, N, d, "bf16", causal, seed=5)
+                r = Runner(w, dev)
+                nn = B * H * N * N * d * (0.5 if causal else 1.0)
+                iters = max(2, int(3e11 / (14 * nn)) + 1)
+                r.fwd()
+                r.dq_rowsum()
+                tf, tq, tk = best(r.fwd, iters), best(r.dq_rowsum, iters), best(r.dkdv, iters)
+                rows.append({"B": B, "H": H, "N": N, "d": d, "causal": causal,
+                             "fwd_tflops": round(4 * nn / tf / 1e9, 1), "bwd_tflops": round(10 * nn / (tq + tk) / 1e9, 1),
+                             "fwd_ms": round(tf, 4), "dq_ms": round(tq, 4), "dkdv_ms": round(tk, 4)})
+                log(f"bench: sweep B={B} H={H} N={N} d={d} causal={causal}")
+                del r
+                torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -737,6 +789,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-fwd-workloads", action="store_true", help="skip the forward-only lines for c1..c4")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the forward, dQ and dK/dV across sequence lengths, head sizes and masks (JSON)")
     ap.add_argument("--variants", action="store_true",
                     help="diagnostic: block-sparse and dropout entry points against dense, one JSON line")
     ap.add_argument("--fwd-workload", default=None,
@@ -790,6 +844,9 @@ def main():
         return
     if args.variants:
         print(json.dumps(time_variants(dev)), flush=True)
+        return
+    if args.sweep:
+        print(json.dumps(time_sweep(dev)), flush=True)
         return
     if args.fwd_workload:
         res = time_fwd_only(args.fwd_workload, dev, iters=args.steps, warmup=args.warmup)
