@@ -43,8 +43,10 @@ struct Bwd16Args {
   float scale;
 };
 
-// Row-fragment reads kept in flight ahead of the S / dP products of the
-// one-wave kernels (all twelve of a 32-row half at d = 128).
+// Row-fragment reads kept in flight ahead of the S / dP products in the dQ
+// kernels that carry dS into the next step (d = 64; d = 128 with dropout or a
+// block mask: twelve of a 32-key half's sixteen) and in the d = 64 dK/dV
+// kernel (all eight of a 32-query half).
 constexpr int kBwdReadAhead = 12;
 
 // Scheduling hint: NM matrix ops with R LDS reads each, the reads issued P
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256, (DqShape<D, SPARSE, DROP>::OCC)) void dq16_ker
 }
 
 // --------------------------------------------------------------------------
-// dK, dV at d = 64 (d = 128 runs dkdv16n_kernel below): a workgroup owns 128
+// dK, dV at d = 64 (d = 128: dkdv16n_kernel, dkdv32s_kernel): a workgroup owns 128
 // keys (32 per wave; K and V rows in VGPRs as the stationary B operands) and
 // streams 64-query tiles of Q and dO, with the query rows' LSE (pre-scaled to
 // log2 units) and D, through LDS.  Per 32-query half: S = Q K^T and
