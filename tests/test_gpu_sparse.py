@@ -91,8 +91,9 @@ def test_bwd_sparse_matches_oracle(dtype, causal, shape, kind):
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_all_ones_mask_is_the_dense_path(dtype):
     """Every block kept: the same arithmetic as fa_fwd / fa_bwd, bit for bit,
-    except dK/dV at d = 128 with 16-bit I/O, where the dense path runs its own
-    kernel (16 keys per wave) that adds the same products in another order:
+    except dK/dV at d = 128 with 16-bit I/O, where the dense path runs a kernel
+    of its own (K and V resident in LDS, 32 keys per wave) and the block-sparse
+    path the 16-key kernel, which add the same products in another order:
     there the two may differ by one rounding of the output type plus fp32
     reordering noise."""
     dev = device()
