@@ -943,8 +943,16 @@ __global__ __launch_bounds__(512, 1) void dkdv32s_kernel(Bwd16Args a) {
   const int g = lane >> 4, col = lane & 15;
   const int Nq = a.Nq, Nk = a.Nk;
 
+  // Heads grouped for 128 workgroups per XCD although an XCD holds 32 of
+  // these: with one workgroup per CU, a group sized to the XCD is one round of
+  // the grid (c5: 8 heads x 32 blocks on 256 CUs), so each round mixed long
+  // and short blocks and the next group's longest ones started late; wider
+  // groups keep the longest-first order across rounds.  Measured (best of 7,
+  // interleaved): c5 dK/dV +3.7 to +4.4%, B=1 H=16 N=8192 causal +1.6%, the
+  // c2 shape +0.3 to +1.2%, long sequences unchanged.  (The two-workgroup
+  // forward and dQ kernels gained nothing from wider groups.)
   int bh, kblk;
-  block_order<32>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
+  block_order<128>(block_id(), a.total, a.nblk, CAUSAL, &bh, &kblk);
   const int kb0 = kblk * KEYS;
   const int kw = kb0 + 32 * kg;
   const Seq sq = seq_of(a.seqlens_q, a.seqlens_k, bh / a.H, Nq, Nk);
