@@ -6,9 +6,11 @@ that are not a multiple of the group size leave a partial last group.  Every
 block's arithmetic is independent of when it runs (no atomics), so all heads
 in one launch must equal the same heads launched one at a time, bit for bit,
 for the forward and each backward stage.  The shapes below give partial
-groups in the forward (12 heads of 64 blocks, groups of 8), in dK/dV and dQ
-(12 and 13 heads of 64 blocks, groups of 8), and head counts that are no
-multiple of 8 in one group (10 heads at N = 2048).
+groups in the forward and dQ (12 heads of 64 blocks, groups of 8), in the
+d = 64 dK/dV and dQ kernels (13 heads of 64 blocks, groups of 8), in the
+d = 128 dK/dV kernel, whose groups are four times wider (20 heads of 64
+128-key blocks, groups of 16), and head counts that are no multiple of 8 in
+one group (10 heads at N = 2048).
 """
 import pytest
 import torch
@@ -19,7 +21,7 @@ from gpu_util import announce, device, to_dev
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(3, 4, 8192, 128, "bf16"), (1, 13, 8192, 64, "f16"), (2, 5, 2048, 128, "bf16")]
+CASES = [(3, 4, 8192, 128, "bf16"), (1, 13, 8192, 64, "f16"), (2, 5, 2048, 128, "bf16"), (1, 20, 8192, 128, "bf16")]
 
 
 @pytest.mark.parametrize("B,H,N,d,dtype", CASES, ids=lambda x: str(x))
